@@ -1,0 +1,202 @@
+"""FP8 (e4m3) codec, block quantisation and the fp8 attention emulation.
+
+TEST INFRASTRUCTURE (see oracle/attention.py).
+
+Sources:
+  * "FlashAttention v1～v4 完整进化史", v3 part 3 (FP8): each block gets its
+    own scale instead of one per tensor (block quantisation); Q and K are both
+    multiplied by one random orthogonal matrix M, which leaves Q K^T unchanged
+    because M M^T = I (incoherent processing); the first product's fp32
+    accumulator is turned into the operand of the second fp8 product, i.e. P
+    itself goes to fp8.
+  * The e4m3 format is not printed on the pages. Reading: the OCP 8-bit
+    "e4m3fn" format - 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent field 0 holds subnormals m/8 * 2^-6; the code with all
+    exponent and mantissa bits set is NaN; there is no infinity; the largest
+    finite magnitude is 448. Encoding rounds to nearest, ties to even, after
+    saturating magnitudes above 448 to 448.
+  * Block granularity is not stated. Reading: one scale per 64 consecutive
+    rows (all d columns) of one (batch, head); s = amax / 448 (s = 1 when the
+    block is all zero). Per-tensor baseline: one s for the whole tensor.
+  * Where a float decides a code (the division x / s), it is taken in
+    float32, the precision the GPU quantiser uses; s itself is
+    float32(amax) / 448 rounded to float32.
+
+Pins: tests/test_oracle_fp8.py (all 65,536 bf16 bit patterns against the
+CPU library cast to float8_e4m3fn, hand-decoded codes, scale properties).
+The tiled fp8 attention emulation follows the pages' steps (it is an
+approximation, not a closed form); its pins are that with P left in float64 it
+reduces to the exact oracle on the dequantised inputs, and that its per-tile P
+rounding stays within the e4m3 half-step bound.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "block_scales",
+           "quantize", "dequantize", "fp8_attention_tiled"]
+
+E4M3_MAX = 448.0
+_MIN_NORMAL_EXP = -6          # 2^-6 is the smallest normal magnitude
+_MANT_BITS = 3
+_BIAS = 7
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Decode e4m3fn codes (uint8) to float64 values."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    sub = m / 8.0 * 2.0 ** _MIN_NORMAL_EXP
+    nor = (1.0 + m / 8.0) * np.exp2((e - _BIAS).astype(np.float64))
+    val = np.where(e == 0, sub, nor) * sign
+    return np.where((e == 0xF) & (m == 0x7), np.nan, val)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Encode values to e4m3fn codes: saturate to +-448, then round to nearest even.
+
+    NaN maps to 0x7F (sign kept). -0.0 keeps its sign bit.
+    """
+    with np.errstate(invalid="ignore"):
+        x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    nan = np.isnan(x)
+    a = np.where(nan, 0.0, a)
+    with np.errstate(divide="ignore"):
+        ex = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    # log2 of values just below a power of two can round up; fix by checking.
+    ex = np.where(np.exp2(ex) > a, ex - 1, ex)
+    ex = np.where(np.exp2(ex + 1) <= a, ex + 1, ex)
+    ex = np.maximum(ex, _MIN_NORMAL_EXP)
+    step = np.exp2(ex - _MANT_BITS)              # spacing of representable values
+    qv = np.rint(a / step) * step                # exact: step is a power of two
+    qv = np.minimum(qv, E4M3_MAX)
+    # Re-encode the rounded magnitude (rounding can carry into the next binade).
+    with np.errstate(divide="ignore"):
+        e2 = np.floor(np.log2(np.where(qv > 0, qv, 1.0)))
+    e2 = np.where(np.exp2(e2) > qv, e2 - 1, e2)
+    e2 = np.where(np.exp2(e2 + 1) <= qv, e2 + 1, e2)
+    is_sub = (qv < 2.0 ** _MIN_NORMAL_EXP)
+    mant_sub = np.rint(qv / 2.0 ** (_MIN_NORMAL_EXP - _MANT_BITS))
+    mant_nor = np.rint((qv / np.exp2(e2) - 1.0) * 8.0)
+    efield = np.where(is_sub, 0, e2 + _BIAS)
+    mfield = np.where(is_sub, mant_sub, mant_nor)
+    code = (efield.astype(np.int64) << 3) | mfield.astype(np.int64)
+    code = np.where(qv == 0, 0, code)
+    code = np.where(nan, 0x7F, code)
+    code = code | np.where(neg, 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def block_scales(x, block_rows: int) -> np.ndarray:
+    """Scales s = amax / 448 in float32 for x of shape [B, H, N, d].
+
+    block_rows > 0: one scale per block of ``block_rows`` rows of each
+    (batch, head), shape [B, H, ceil(N / block_rows)]. block_rows == 0: one
+    scale for the whole tensor, returned broadcast to shape [B, H, ceil(N/64)].
+    An all-zero block gets s = 1.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    B, H, N, _ = x.shape
+    nb64 = -(-N // 64)
+    if block_rows == 0:
+        amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+        s = np.float32(amax) / np.float32(E4M3_MAX)
+        if amax == 0:
+            s = np.float32(1.0)
+        return np.full((B, H, nb64), s, dtype=np.float32)
+    nb = -(-N // block_rows)
+    out = np.empty((B, H, nb), dtype=np.float32)
+    for i in range(nb):
+        blk = np.abs(x[:, :, i * block_rows:(i + 1) * block_rows, :])
+        amax = blk.max(axis=(2, 3)).astype(np.float32)
+        s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        out[:, :, i] = np.where(amax == 0, np.float32(1.0), s)
+    return out
+
+
+def _expand_rows(s, N, block_rows):
+    idx = np.arange(N) // block_rows
+    return s[:, :, idx]
+
+
+def quantize(x, block_rows: int, rot=None):
+    """Quantise x [B, H, N, d] to e4m3 codes with per-block scales.
+
+    With ``rot`` (d x d), x is first multiplied by it on the right, in
+    float64, and the product rounded to float32 (the GPU forms it in float32
+    in a different summation order; codes are compared with that in mind).
+    The division x / s is taken in float32. Returns (codes uint8, scales f32,
+    the float32 values that were quantised).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if rot is not None:
+        x = x @ np.asarray(rot, dtype=np.float64)
+    xf = x.astype(np.float32)
+    s = block_scales(xf, block_rows)
+    br = block_rows if block_rows > 0 else 64
+    srow = _expand_rows(s, xf.shape[2], br)[..., None].astype(np.float32)
+    y = (xf / srow).astype(np.float32)
+    return e4m3_encode(y), s, xf
+
+
+def dequantize(codes, scales, block_rows: int = 64) -> np.ndarray:
+    """Dequantised float64 values: decode(code) * s of the code's row block."""
+    c = np.asarray(codes)
+    br = block_rows if block_rows > 0 else 64
+    srow = _expand_rows(np.asarray(scales, dtype=np.float64), c.shape[2], br)[..., None]
+    return e4m3_decode(c) * srow
+
+
+def fp8_attention_tiled(q8, sq, k8, sk, v8, sv, scale: float, causal: bool,
+                        B_c: int = 64, quantize_p: bool = True, block_rows: int = 64):
+    """fp8 attention following the pages' tiled steps, in float64.
+
+    Inputs are e4m3 codes with per-block scales. For each key tile of B_c
+    keys: S = scale * Q K^T on the dequantised values, the online max and sum
+    update, P~ = exp(S - m_new); the sum l uses P~ itself while the product
+    with V uses P~ rounded through e4m3 as e4m3(P~ * 448) / 448 (taken in
+    float32, the precision the GPU forms P~ in). O = sum / l at the end.
+
+    With quantize_p=False the P rounding is skipped and the result equals the
+    exact attention of the dequantised inputs (a pin).
+    Returns (O, LSE) float64, shapes [B, H, N, d] and [B, H, N].
+    """
+    qd = dequantize(q8, sq, block_rows)
+    kd = dequantize(k8, sk, block_rows)
+    vd = dequantize(v8, sv, block_rows)
+    B, H, N, d = qd.shape
+    o_all = np.zeros_like(qd)
+    lse_all = np.empty((B, H, N))
+    t_c = -(-N // B_c)
+    for b in range(B):
+        for h in range(H):
+            q, k, v = qd[b, h], kd[b, h], vd[b, h]
+            m = np.full(N, -np.inf)
+            l = np.zeros(N)
+            o = np.zeros((N, d))
+            for j in range(t_c):
+                c0, c1 = j * B_c, min(N, (j + 1) * B_c)
+                s = scale * (q @ k[c0:c1].T)
+                if causal:
+                    s = np.where(np.arange(c0, c1)[None, :] > np.arange(N)[:, None], -np.inf, s)
+                m_new = np.maximum(m, s.max(axis=1))
+                live = np.isfinite(m_new)
+                m_ref = np.where(live, m_new, 0.0)
+                alpha = np.where(live, np.exp(m - m_ref), 0.0)
+                p = np.where(live[:, None], np.exp(s - m_ref[:, None]), 0.0)
+                l = alpha * l + p.sum(axis=1)
+                if quantize_p:
+                    p32 = p.astype(np.float32) * np.float32(E4M3_MAX)
+                    pv = e4m3_decode(e4m3_encode(p32)) / E4M3_MAX
+                else:
+                    pv = p
+                o = alpha[:, None] * o + pv @ v[c0:c1]
+                m = m_new
+            o_all[b, h] = o / np.where(l > 0, l, 1.0)[:, None]
+            lse_all[b, h] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return o_all, lse_all

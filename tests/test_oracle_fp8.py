@@ -1,0 +1,138 @@
+"""Pins of the oracle's e4m3 codec, block quantiser and fp8 attention emulation."""
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import fp8 as F
+from seeded_inputs import bf16_bits_to_f32
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def test_decode_all_codes_against_torch():
+    torch = _torch()
+    codes = np.arange(256, dtype=np.uint8)
+    ours = F.e4m3_decode(codes)
+    theirs = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().double().numpy()
+    both_nan = np.isnan(ours) & np.isnan(theirs)
+    assert np.all(both_nan | (ours == theirs))
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF]) and np.sum(np.isnan(ours)) == 2
+
+
+def test_known_codes():
+    assert F.e4m3_decode(np.uint8(0x7E)) == 448.0        # largest finite
+    assert F.e4m3_decode(np.uint8(0x38)) == 1.0
+    assert F.e4m3_decode(np.uint8(0x08)) == 2.0 ** -6    # smallest normal
+    assert F.e4m3_decode(np.uint8(0x01)) == 2.0 ** -9    # smallest subnormal
+    assert F.e4m3_decode(np.uint8(0xC0)) == -2.0
+    assert F.e4m3_encode(np.array([448.0, 1e9, -1e9, 464.0, 0.0]))[:5].tolist() == \
+        [0x7E, 0x7E, 0xFE, 0x7E, 0x00]
+
+
+def test_encode_every_bf16_pattern_against_torch():
+    """All 65,536 bf16 bit patterns, cast through float32, against torch's cast.
+
+    torch's cast does not saturate (magnitudes from 464 up become NaN), so
+    those inputs are checked against saturation to +-448 instead.
+    """
+    torch = _torch()
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = bf16_bits_to_f32(bits)
+    ours = F.e4m3_encode(x)
+    theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    finite_small = np.isfinite(x) & (np.abs(x) < 464.0)
+    assert np.array_equal(ours[finite_small], theirs[finite_small])
+    big = np.isfinite(x) & (np.abs(x) >= 464.0)
+    assert np.all((ours[big] & 0x7F) == 0x7E)
+    assert np.all((ours[big] >> 7) == (x[big] < 0))
+    nan = np.isnan(x)
+    assert np.all((ours[nan] & 0x7F) == 0x7F)
+    inf = np.isinf(x)
+    assert np.all((ours[inf] & 0x7F) == 0x7E)
+
+
+def test_roundtrip_error_is_half_step():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal(100000) * 50
+    x = np.clip(x, -448, 448)
+    y = F.e4m3_decode(F.e4m3_encode(x))
+    a = np.abs(x)
+    ex = np.maximum(np.floor(np.log2(np.maximum(a, 1e-300))), -6)
+    half_step = np.exp2(ex - 3) / 2
+    assert np.all(np.abs(y - x) <= half_step * (1 + 1e-12))
+
+
+def test_block_scales_and_codes():
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((2, 3, 150, 16)).astype(np.float32)
+    x[1, 2, 64:128] = 0.0
+    codes, s, xf = F.quantize(x, 64)
+    assert s.shape == (2, 3, 3)
+    assert s[1, 2, 1] == 1.0
+    for b in range(2):
+        for h in range(3):
+            for i in range(3):
+                blk = xf[b, h, 64 * i:64 * (i + 1)]
+                amax = np.float32(np.abs(blk).max())
+                if amax > 0:
+                    assert s[b, h, i] == np.float32(amax / np.float32(448.0))
+                    # the largest element maps to the largest code
+                    cblk = codes[b, h, 64 * i:64 * (i + 1)]
+                    assert np.max(cblk & 0x7F) == 0x7E
+    d = F.dequantize(codes, s, 64)
+    srow = s[:, :, np.arange(150) // 64][..., None]
+    assert np.all(np.abs(d - x) <= srow * 448 * 2.0 ** -4 + 1e-30)
+    # per-tensor: one scale everywhere
+    c0, s0, _ = F.quantize(x, 0)
+    assert np.all(s0 == s0.flat[0])
+    assert s0.flat[0] == np.float32(np.float32(np.abs(x).max()) / np.float32(448))
+
+
+def test_rotation_leaves_scores_unchanged_before_rounding():
+    rng = np.random.default_rng(33)
+    d = 16
+    m, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    q = rng.standard_normal((1, 1, 64, d))
+    k = rng.standard_normal((1, 1, 64, d))
+    _, _, qr_ = F.quantize(q, 64, rot=m)
+    _, _, kr_ = F.quantize(k, 64, rot=m)
+    s1 = qr_[0, 0].astype(np.float64) @ kr_[0, 0].astype(np.float64).T
+    s2 = q[0, 0] @ k[0, 0].T
+    assert np.max(np.abs(s1 - s2)) <= 1e-4
+
+
+def test_fp8_emulation_without_p_rounding_is_exact_attention():
+    rng = np.random.default_rng(34)
+    x = {n: rng.standard_normal((1, 2, 130, 16)) for n in "qkv"}
+    qc = {n: F.quantize(x[n], 64) for n in "qkv"}
+    for causal in (False, True):
+        o, lse = F.fp8_attention_tiled(qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1],
+                                       qc["v"][0], qc["v"][1], 0.25, causal, B_c=64,
+                                       quantize_p=False)
+        deq = {n: F.dequantize(qc[n][0], qc[n][1], 64) for n in "qkv"}
+        o_ref, l_ref = A.forward(deq["q"], deq["k"], deq["v"], 0.25, causal)
+        assert np.max(np.abs(o - o_ref)) <= 1e-12
+        assert np.max(np.abs(lse - l_ref)) <= 1e-12
+
+
+def test_fp8_emulation_p_rounding_within_bound():
+    """Rounding P~ * 448 to e4m3 moves each weight by at most half a step.
+
+    |P8 - P~| <= 2^-4 P~ + 2^-10 / 448 per weight, so each O element moves by
+    at most (2^-4 + 2^-10 / 448 * n_keys / l) * max|v| (ratios with l >= 1).
+    """
+    rng = np.random.default_rng(35)
+    x = {n: rng.standard_normal((1, 1, 192, 16)) for n in "qkv"}
+    qc = {n: F.quantize(x[n], 64) for n in "qkv"}
+    args = (qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1], qc["v"][0], qc["v"][1], 0.25, False)
+    o8, l8 = F.fp8_attention_tiled(*args, B_c=64, quantize_p=True)
+    o, l = F.fp8_attention_tiled(*args, B_c=64, quantize_p=False)
+    vmax = np.abs(F.dequantize(qc["v"][0], qc["v"][1], 64)).max()
+    bound = (2.0 ** -4 + 2.0 ** -10 / 448 * 192) * vmax
+    assert np.max(np.abs(o8 - o)) <= bound
+    assert np.max(np.abs(o8 - o)) > 0          # the rounding is really applied
+    assert np.array_equal(l8, l)                # l comes from the unrounded P~
