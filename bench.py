@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Attention throughput on one MI355X: TFLOP/s and fraction of the bf16 MFMA peak.
+
+One step = one pass of the hot path over the long-context causal workload
+(B=1, H=32, N=16384, d=128, bf16): the fused forward (O and LSE) followed by
+the recompute-based backward (dQ, dK, dV). Inputs are seeded synthetic
+N(0, 1) tensors already resident in device memory.
+
+FLOP convention: forward 4*B*H*N^2*d, backward 2.5x forward (five matrix
+products), halved for the causal mask.
+
+Prints one JSON line. ``--gpus N`` with N > 1 is refused: this build runs on
+one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "exact_tiled_attention_12_amd", "csrc")
+
+
+def attention_flops(B, H, N, d, causal, backward=False):
+    f = 4.0 * B * H * N * N * d
+    if causal:
+        f *= 0.5
+    return f * (2.5 if backward else 1.0)
+
+
+def kernel_source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, files, per_launch_units):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if current."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("src_sha") != kernel_source_sha(files):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(heads: int):
+    """The float64 oracle, timed on this host on a bounded sample of the workload."""
+    import numpy as np
+    import seeded_inputs as si
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = si.workload(4)
+    rng = np.random.default_rng(w.seed)
+    shape = (w.N, w.d)
+    x = {n: si.bf16_round(rng.standard_normal(size=shape, dtype=np.float32))[1] for n in ("q", "k", "v", "do")}
+    t0 = time.perf_counter()
+    for _ in range(heads):
+        A.forward(x["q"], x["k"], x["v"], w.scale, True)
+        A.backward(x["q"], x["k"], x["v"], x["do"], w.scale, True)
+    dt = time.perf_counter() - t0
+    flops = heads * (attention_flops(1, 1, w.N, w.d, True) + attention_flops(1, 1, w.N, w.d, True, True))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} head(s) of the N=16384 d=128 causal workload, forward + backward, "
+                      f"float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the attention of each (batch, head) is independent; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import exact_tiled_attention_12_amd as fa
+    import seeded_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load()
+    w = si.workload(4)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    x = si.make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def t(n):
+        return torch.from_numpy(x[n + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (t(n) for n in ("q", "k", "v", "do"))
+    del x
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), device=dev, dtype=torch.uint8)
+    do_bwd = not args.fwd_only
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+        if ev:
+            ev[1].record()
+        if do_bwd:
+            fa.bwd(q, k, v, o, lse, do, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
+            if ev:
+                ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if do_bwd else 0.0
+    ms_per_step = wall * 1e3 / args.steps
+
+    f_fwd = attention_flops(B, H, N, d, True)
+    f_bwd = attention_flops(B, H, N, d, True, True) if do_bwd else 0.0
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+
+    # Roofline of the dominant kernel: algorithmic FLOPs per launch / its event-timed duration.
+    if do_bwd and bwd_ms > fwd_ms:
+        dom, dom_ms, dom_flops, files = "attn_bwd", bwd_ms, f_bwd, ["fa_bwd.hip", "fa_device.h"]
+    else:
+        dom, dom_ms, dom_flops, files = "attn_fwd", fwd_ms, f_fwd, ["fa_fwd.hip", "fa_device.h"]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic(f"{dom}_bf16_d128_causal_N16384_B1_H32", files, 1)}
+
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s at d=128 causal bf16, % of MFMA peak (1 GPU)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal bf16 attention, B=1 H=32 N=16384 d=128, "
+                               + ("forward only" if args.fwd_only else "forward + backward"),
+                   "B": B, "H": H, "N": N, "d": d, "causal": True},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "breakdown": {"fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                      "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+                      "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if do_bwd else None},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+"""Python binding over the C ABI: argument marshalling only.
+
+torch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's kernels. Shapes are [B, H, N, d].
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "quant_fp8", "fwd_fp8"]
+
+
+def _stream(t: torch.Tensor):
+    return ctypes_ptr(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def ctypes_ptr(x: int):
+    return x if x else None
+
+
+def _check_tensor(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _shape4(q: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError(f"expected a [B, H, N, d] tensor, got shape {tuple(q.shape)}")
+    return tuple(int(x) for x in q.shape)
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """O, LSE = attention(q, k, v). bf16 or float32 inputs; O has the input dtype."""
+    B, H, N, d = _shape4(q)
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"q must be bfloat16 or float32 (got {dt})")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, dt, (B, H, N, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    _check_tensor(out, "out", dt, (B, H, N, d))
+    _check_tensor(lse, "lse", torch.float32, (B, H, N))
+    lib = _lib.load()
+    fn = lib.fa_fwd if dt == torch.bfloat16 else lib.fa_fwd_f32
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, H, N, d, float(scale), int(bool(causal)), _stream(q))
+    _lib.check(st, "fa_fwd" if dt == torch.bfloat16 else "fa_fwd_f32")
+    return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.load().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
+        workspace=None, dq=None, dk=None, dv=None):
+    """dQ, dK, dV of sum(O * dO), recomputing P from LSE. bf16 or float32."""
+    B, H, N, d = _shape4(q)
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check_tensor(t, n, dt, (B, H, N, d))
+    _check_tensor(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_tensor(t, n, dt, (B, H, N, d))
+    lib = _lib.load()
+    fn = lib.fa_bwd if dt == torch.bfloat16 else lib.fa_bwd_f32
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(),
+            B, H, N, d, float(scale), int(bool(causal)), _stream(q))
+    _lib.check(st, "fa_bwd" if dt == torch.bfloat16 else "fa_bwd_f32")
+    return dq, dk, dv
+
+
+def quant_fp8(x, rot=None, block_rows: int = 64, x8=None, scales=None):
+    """e4m3 codes (uint8) and per-64-row float32 scales of x (bf16 [B,H,N,d])."""
+    B, H, N, d = _shape4(x)
+    _check_tensor(x, "x", torch.bfloat16, (B, H, N, d))
+    if rot is not None:
+        _check_tensor(rot, "rot", torch.float32, (d, d))
+    x8 = torch.empty((B, H, N, d), device=x.device, dtype=torch.uint8) if x8 is None else x8
+    nb = (N + 63) // 64
+    scales = torch.empty((B, H, nb), device=x.device, dtype=torch.float32) if scales is None else scales
+    _check_tensor(x8, "x8", torch.uint8, (B, H, N, d))
+    _check_tensor(scales, "scales", torch.float32, (B, H, nb))
+    st = _lib.load().fa_quant_fp8(x.data_ptr(), rot.data_ptr() if rot is not None else None,
+                                  x8.data_ptr(), scales.data_ptr(), B, H, N, d, int(block_rows), _stream(x))
+    _lib.check(st, "fa_quant_fp8")
+    return x8, scales
+
+
+def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """O (bf16), LSE from e4m3 codes with per-64-row scales."""
+    B, H, N, d = _shape4(q8)
+    nb = (N + 63) // 64
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _check_tensor(t, n, torch.uint8, (B, H, N, d))
+    for t, n in ((sq, "sq"), (sk, "sk"), (sv, "sv")):
+        _check_tensor(t, n, torch.float32, (B, H, nb))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((B, H, N, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
+    lse = torch.empty((B, H, N), device=q8.device, dtype=torch.float32) if lse is None else lse
+    st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), sq.data_ptr(), sk.data_ptr(),
+                                sv.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
+                                int(bool(causal)), _stream(q8))
+    _lib.check(st, "fa_fwd_fp8")
+    return out, lse

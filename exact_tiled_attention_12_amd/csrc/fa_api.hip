@@ -1,0 +1,198 @@
+// C ABI of the library: argument checks, then one asynchronous launch
+// sequence on the caller's stream. See include/fa.h for the contract.
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return FA_OK;
+}
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+  const char* name;
+  size_t align;
+};
+
+bool overlaps(const Buf& a, const Buf& b) {
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Sizes, head dimension and scale.
+int check_shape(int B, int H, int N, int d, float scale) {
+  if (B < 1 || H < 1 || N < 1)
+    return fail(FA_ERR_INVALID, "B, H and N must be >= 1 (got B=%d H=%d N=%d)", B, H, N);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d must be 64 or 128 (got %d)", d);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(FA_ERR_UNSUPPORTED, "scale must be finite and >= 0 (got %g)", (double)scale);
+  const long long tiles = (long long)B * H * ((N + 63) / 64);
+  if (tiles > INT_MAX / 2 || (long long)B * H * N > INT_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "problem too large: B*H*N = %lld exceeds the supported range",
+                (long long)B * H * N);
+  return FA_OK;
+}
+
+// Null, alignment and overlap checks. inputs/outputs are arrays of n buffers.
+int check_bufs(const Buf* in, int n_in, const Buf* out, int n_out) {
+  for (int i = 0; i < n_in + n_out; ++i) {
+    const Buf& b = i < n_in ? in[i] : out[i - n_in];
+    if (b.p == nullptr) return fail(FA_ERR_INVALID, "%s is NULL", b.name);
+    if ((uintptr_t)b.p % b.align != 0)
+      return fail(FA_ERR_UNSUPPORTED, "%s must be %zu-byte aligned", b.name, b.align);
+  }
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlaps(out[i], in[j]))
+        return fail(FA_ERR_INVALID, "output %s overlaps input %s", out[i].name, in[j].name);
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(out[i], out[j]))
+        return fail(FA_ERR_INVALID, "outputs %s and %s overlap", out[i].name, out[j].name);
+  }
+  return FA_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+float log2e_scale(float scale) { return (float)((double)scale * 1.4426950408889634); }
+
+int fwd_common(fa::DType dt, const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, void* stream) {
+  int rc = check_shape(B, H, N, d, scale);
+  if (rc) return rc;
+  const size_t e = dt == fa::DType::BF16 ? 2 : 4;
+  const size_t tb = (size_t)B * H * N * d * e, lb = (size_t)B * H * N * 4;
+  const Buf in[3] = {{q, tb, "q", 16}, {k, tb, "k", 16}, {v, tb, "v", 16}};
+  const Buf out[2] = {{o, tb, "o", 16}, {lse, lb, "lse", 4}};
+  rc = check_bufs(in, 3, out, 2);
+  if (rc) return rc;
+  fa::FwdArgs a{q, k, v, o, lse, N, 0, log2e_scale(scale), 0};
+  return launched(fa::launch_fwd(dt, d, causal, a, B, H, (hipStream_t)stream), "attention forward");
+}
+
+int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, int B, int H, int N,
+               int d, float scale, int causal, void* stream) {
+  int rc = check_shape(B, H, N, d, scale);
+  if (rc) return rc;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  if (ws == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
+  if ((uintptr_t)ws % 256 != 0) return fail(FA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(FA_ERR_INVALID, "workspace has %zu bytes, needs fa_bwd_workspace_bytes() = %zu", ws_bytes, need);
+  const size_t e = dt == fa::DType::BF16 ? 2 : 4;
+  const size_t tb = (size_t)B * H * N * d * e, lb = (size_t)B * H * N * 4;
+  const Buf in[6] = {{q, tb, "q", 16},   {k, tb, "k", 16},     {v, tb, "v", 16},
+                     {o, tb, "o", 16},   {lse, lb, "lse", 4},  {dout, tb, "dout", 16}};
+  const Buf out[4] = {{dq, tb, "dq", 16}, {dk, tb, "dk", 16}, {dv, tb, "dv", 16}, {ws, need, "workspace", 256}};
+  rc = check_bufs(in, 6, out, 4);
+  if (rc) return rc;
+  const size_t acc_bytes = align256((size_t)B * H * N * d * 4);
+  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)ws, (float*)((char*)ws + acc_bytes),
+                N, 0, scale, log2e_scale(scale), 0};
+  return launched(fa::launch_bwd(dt, d, causal, a, B, H, (hipStream_t)stream), "attention backward");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported argument";
+    case FA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, void* stream) {
+  return fwd_common(fa::DType::BF16, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+  return fwd_common(fa::DType::F32, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  return align256((size_t)B * H * N * d * 4) + align256((size_t)B * H * N * 4);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+           float scale, int causal, void* stream) {
+  return bwd_common(fa::DType::BF16, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                    scale, causal, stream);
+}
+
+int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
+               const float* dout, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, int B,
+               int H, int N, int d, float scale, int causal, void* stream) {
+  return bwd_common(fa::DType::F32, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                    scale, causal, stream);
+}
+
+int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, float* scales, int B, int H, int N, int d,
+                 int block_rows, void* stream) {
+  int rc = check_shape(B, H, N, d, 1.f);
+  if (rc) return rc;
+  if (block_rows != 64 && block_rows != 0)
+    return fail(FA_ERR_UNSUPPORTED, "block_rows must be 64 or 0 (got %d)", block_rows);
+  const size_t n = (size_t)B * H * N * d;
+  const size_t sb = (size_t)B * H * ((N + 63) / 64) * 4;
+  const Buf in_r[2] = {{x, n * 2, "x", 16}, {rot, (size_t)d * d * 4, "rot", 16}};
+  const Buf out[2] = {{x8, n, "x8", 16}, {scales, sb, "scales", 4}};
+  rc = check_bufs(in_r, rot ? 2 : 1, out, 2);
+  if (rc) return rc;
+  fa::QuantArgs a{x, rot, x8, scales, N, block_rows};
+  return launched(fa::launch_quant_fp8(d, a, B, H, (hipStream_t)stream), "fp8 quantisation");
+}
+
+int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* v8, const float* sq,
+               const float* sk, const float* sv, void* o, float* lse, int B, int H, int N, int d, float scale,
+               int causal, void* stream) {
+  int rc = check_shape(B, H, N, d, scale);
+  if (rc) return rc;
+  if (d != 128) return fail(FA_ERR_UNSUPPORTED, "fp8 forward supports d = 128 only (got %d)", d);
+  const size_t n = (size_t)B * H * N * d;
+  const size_t sb = (size_t)B * H * ((N + 63) / 64) * 4;
+  const Buf in[6] = {{q8, n, "q8", 16}, {k8, n, "k8", 16}, {v8, n, "v8", 16},
+                     {sq, sb, "sq", 4},  {sk, sb, "sk", 4},  {sv, sb, "sv", 4}};
+  const Buf out[2] = {{o, n * 2, "o", 16}, {lse, (size_t)B * H * N * 4, "lse", 4}};
+  rc = check_bufs(in, 6, out, 2);
+  if (rc) return rc;
+  fa::Fp8FwdArgs a{q8, k8, v8, sq, sk, sv, o, lse, N, 0, log2e_scale(scale), 0};
+  return launched(fa::launch_fwd_fp8(d, causal, a, B, H, (hipStream_t)stream), "fp8 attention forward");
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) fused exact-attention library.
+ *
+ * The library computes O = softmax(scale * Q K^T) V one (batch, head, query
+ * tile) per workgroup with the online softmax, so that the N x N score and
+ * probability matrices never reach device memory, and it saves one
+ * log-sum-exp per row for the recompute-based backward.
+ *
+ * What the calls compute follows these pages:
+ *   - "FlashAttention v1～v4 完整进化史" (qscqesze), section "第一层地基":
+ *     S = Q K^T / sqrt(d), P = softmax(S), O = P V;
+ *   - "6.1 FlashAttention V1详解" (AIInfraGuide), section 8.1: tensors are
+ *     [B, H, N, D] and the per-row statistics are [B, H, N];
+ *   - "FlashAttention v1～v4 完整进化史", v2 part 1: the saved statistic is
+ *     L = m + log(l);
+ *   - "6.1 FlashAttention V1详解", sections 6.1-6.2: the backward recomputes
+ *     S and P from Q, K and the saved statistic instead of storing them;
+ *   - "FlashAttention v1～v4 完整进化史", v3 part 3: fp8 with a scale per
+ *     block and Q, K rotated by one random orthogonal matrix.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device. The
+ *     caller owns every buffer; the library never allocates, frees or
+ *     synchronises, and keeps no state apart from a thread-local error text.
+ *   - Layout: contiguous row-major [B, H, N, d] for Q, K, V, O and the
+ *     gradients; [B, H, N] float32 for LSE. B and H are batch dimensions.
+ *   - d must be 64 or 128. B, H, N >= 1. scale must be finite and >= 0
+ *     (the workloads use 1/sqrt(d)).
+ *   - causal != 0 applies the lower-triangular mask: query i sees keys
+ *     j <= i (the diagonal is kept). N queries and N keys.
+ *   - LSE is the natural log of sum_j exp(scale * q_i . k_j) over the keys
+ *     query i sees.
+ *   - Tensor pointers must be 16-byte aligned; LSE and scale arrays 4-byte.
+ *   - Outputs must not overlap inputs. Inputs are only read; outputs are
+ *     fully overwritten.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work and returns; results are ready when the
+ *     stream reaches them.
+ *   - Errors: every argument is checked before anything is enqueued; on a
+ *     non-zero return nothing was enqueued (FA_ERR_HIP: a launch failed,
+ *     earlier launches of the same call may have been enqueued).
+ *     fa_last_error() then describes the failure.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point is exported from the shared library (which is built with
+ * hidden default visibility). */
+#define FA_API __attribute__((visibility("default")))
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID = -1,     /* null pointer, a size < 1, overlapping buffers, workspace too small */
+    FA_ERR_UNSUPPORTED = -2, /* d not 64/128, scale negative or not finite, misaligned pointer, size too large */
+    FA_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
+};
+
+/* Forward, bf16 inputs and output (bits of bfloat16 in 2-byte elements).
+ * q, k, v: [B,H,N,d] bf16. o: [B,H,N,d] bf16 (written). lse: [B,H,N] float (written).
+ * Scores and the output accumulator are float32; P is rounded to bf16
+ * (nearest-even) before it multiplies V; O is rounded to bf16 once. */
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Forward, float32 inputs and output. Same contract as fa_fwd; every product
+ * and sum is in float32 (P is not rounded). */
+FA_API int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Bytes of device workspace fa_bwd / fa_bwd_f32 need: a float32 dQ
+ * accumulator [B,H,N,d] and D = rowsum(dO * O) [B,H,N] float32, each
+ * rounded up to 256 bytes. Linear in N (no N x N buffer). Returns 0 for
+ * invalid sizes. */
+FA_API size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward, bf16. Given the forward's inputs q, k, v, its outputs o and lse,
+ * and dout = dL/dO, writes dq, dk, dv = dL/dQ, dL/dK, dL/dV (bf16):
+ *   D_i = sum_c dO_ic O_ic,  P = exp(scale Q K^T - LSE) (recomputed),
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,
+ *   dK = scale dS^T Q.
+ * workspace: device memory of at least fa_bwd_workspace_bytes(B,H,N,d)
+ * bytes, 256-byte aligned; its contents are undefined on entry and exit.
+ * dQ is accumulated with float32 atomics, so dq may differ in the last bits
+ * between runs; dk and dv are deterministic. */
+FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Backward, float32 tensors. Same contract as fa_bwd. */
+FA_API int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
+               const float* dout, float* dq, float* dk, float* dv,
+               void* workspace, size_t workspace_bytes,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* fp8 quantisation ("FlashAttention v1～v4 完整进化史", v3 part 3).
+ * x: [B,H,N,d] bf16. rot: d x d float32 row-major orthogonal matrix or NULL;
+ * with rot the quantised tensor is x * rot (float32 products and sums).
+ * block_rows = 64: one scale per 64 rows x d of each (b,h);
+ * block_rows = 0: one scale for the whole tensor (the per-tensor baseline).
+ * scales: [B,H,ceil(N/64)] float32 (written; with block_rows = 0 every entry
+ * holds the same value). s = amax / 448 in float32 (1 for an all-zero block);
+ * x8 = e4m3fn(x / s), round to nearest even after saturating to +-448
+ * (x8: [B,H,N,d] bytes, written). NaN inputs give the NaN code.
+ * block_rows = 0 uses scales as scratch for a two-pass reduction. */
+FA_API int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, float* scales,
+                 int B, int H, int N, int d, int block_rows, void* stream);
+
+/* Forward on fp8 inputs: q8, k8, v8 e4m3fn codes [B,H,N,d] with scales
+ * sq, sk, sv [B,H,ceil(N/64)] as written by fa_quant_fp8 (the dequantised
+ * value of a code is decode(code) * s of its 64-row block). Both products
+ * run on fp8 MFMA with float32 accumulation; P~ = exp(S - m) is rounded to
+ * e4m3 as e4m3(P~ * 448) for the product with V, while the row sum l uses
+ * the float32 P~. o: [B,H,N,d] bf16 (written). lse: [B,H,N] float32. d must
+ * be 128. */
+FA_API int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* v8,
+               const float* sq, const float* sk, const float* sv,
+               void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Static text for a status code. */
+FA_API const char* fa_status_string(int status);
+
+/* Thread-local description of the last non-OK return on this thread ("" if none). */
+FA_API const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

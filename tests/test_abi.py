@@ -1,0 +1,130 @@
+"""The C ABI on the CPU: the library loads, exports every declared call, and
+rejects bad arguments before anything reaches the GPU.
+
+Every call here fails validation, so no kernel is launched and no GPU is needed.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_12_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+A = 0x100000          # fake, 256-byte aligned device addresses (never dereferenced)
+GAP = 1 << 32
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:FA_API\s+)?(?:const\s+)?[a-z_]+\s*\*?\s*(fa_[a-z0-9_]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libfa_mi355x.so is not built; run python -m exact_tiled_attention_12_amd.build")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.FAError):
+        _lib.load(str(tmp_path / "nope.so"))
+
+
+def _fwd(lib, q=A, k=A + GAP, v=A + 2 * GAP, o=A + 3 * GAP, lse=A + 4 * GAP,
+         B=1, H=1, N=16, d=64, scale=0.125, causal=0, f32=False):
+    fn = lib.fa_fwd_f32 if f32 else lib.fa_fwd
+    return fn(q, k, v, o, lse, B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), _lib.FA_ERR_INVALID),
+    (dict(H=-1), _lib.FA_ERR_INVALID),
+    (dict(N=0), _lib.FA_ERR_INVALID),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=256), _lib.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), _lib.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("inf")), _lib.FA_ERR_UNSUPPORTED),
+    (dict(scale=-0.5), _lib.FA_ERR_UNSUPPORTED),
+    (dict(q=None), _lib.FA_ERR_INVALID),
+    (dict(lse=None), _lib.FA_ERR_INVALID),
+    (dict(q=A + 8), _lib.FA_ERR_UNSUPPORTED),
+    (dict(lse=A + 4 * GAP + 2), _lib.FA_ERR_UNSUPPORTED),
+    (dict(o=A + 256), _lib.FA_ERR_INVALID),                 # o overlaps q
+    (dict(lse=A + 3 * GAP + 64), _lib.FA_ERR_INVALID),      # lse inside o
+    (dict(B=1 << 16, H=1 << 12, N=1 << 12), _lib.FA_ERR_UNSUPPORTED),
+])
+@pytest.mark.parametrize("f32", [False, True])
+def test_forward_rejects(lib, kw, status, f32):
+    assert _fwd(lib, f32=f32, **kw) == status
+    msg = lib.fa_last_error().decode()
+    assert msg, "a failed call must leave a reason"
+
+
+def test_error_text_names_the_argument(lib):
+    assert _fwd(lib, d=80) == _lib.FA_ERR_UNSUPPORTED
+    assert "80" in lib.fa_last_error().decode()
+    assert _fwd(lib, q=None) == _lib.FA_ERR_INVALID
+    assert "q" in lib.fa_last_error().decode()
+    for st in (0, -1, -2, -3, 7):
+        assert lib.fa_status_string(st)
+
+
+def test_workspace_is_linear_in_n(lib):
+    def ws(B, H, N, d):
+        return lib.fa_bwd_workspace_bytes(B, H, N, d)
+    def al(x):
+        return (x + 255) // 256 * 256
+    for (B, H, N, d) in [(1, 1, 1, 64), (2, 3, 1000, 128), (1, 32, 16384, 128)]:
+        assert ws(B, H, N, d) == al(4 * B * H * N * d) + al(4 * B * H * N)
+    assert ws(1, 32, 16384, 128) < 300 * 2 ** 20     # far below one N x N fp32 matrix (1 GiB)
+    assert ws(0, 1, 1, 64) == 0 and ws(1, 1, 1, 100) == 0
+
+
+def _bwd(lib, ws=A + 10 * GAP, ws_bytes=None, B=1, H=1, N=16, d=64, scale=0.125, **over):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    p = dict(q=A, k=A + GAP, v=A + 2 * GAP, o=A + 3 * GAP, lse=A + 4 * GAP, do=A + 5 * GAP,
+             dq=A + 6 * GAP, dk=A + 7 * GAP, dv=A + 8 * GAP)
+    p.update(over)
+    return lib.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                      ws, ws_bytes, B, H, N, d, scale, 1, None)
+
+
+def test_backward_rejects(lib):
+    assert _bwd(lib, ws=None) == _lib.FA_ERR_INVALID
+    assert _bwd(lib, ws_bytes=100) == _lib.FA_ERR_INVALID
+    assert _bwd(lib, ws=A + 10 * GAP + 16) == _lib.FA_ERR_UNSUPPORTED
+    assert _bwd(lib, dq=A + 64) == _lib.FA_ERR_INVALID           # dq overlaps q
+    assert _bwd(lib, dk=A + 6 * GAP) == _lib.FA_ERR_INVALID      # dk aliases dq
+    assert _bwd(lib, d=32) == _lib.FA_ERR_UNSUPPORTED
+    assert _bwd(lib, do=None) == _lib.FA_ERR_INVALID
+
+
+def test_fp8_rejects(lib):
+    q = A
+    assert lib.fa_quant_fp8(q, None, A + GAP, A + 2 * GAP, 1, 1, 64, 128, 32, None) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_quant_fp8(q, None, None, A + 2 * GAP, 1, 1, 64, 128, 64, None) == _lib.FA_ERR_INVALID
+    assert lib.fa_quant_fp8(q, None, A + 256, A + 2 * GAP, 1, 1, 64, 128, 64, None) == _lib.FA_ERR_INVALID
+    s = A + 3 * GAP
+    assert lib.fa_fwd_fp8(A, A + GAP, A + 2 * GAP, s, s + GAP, s + 2 * GAP, s + 3 * GAP, s + 4 * GAP,
+                          1, 1, 64, 64, 0.125, 0, None) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_fwd_fp8(A, A + GAP, A + 2 * GAP, s, s + GAP, s + 2 * GAP, A + 256, s + 4 * GAP,
+                          1, 1, 64, 128, 0.125, 0, None) == _lib.FA_ERR_INVALID
