@@ -125,20 +125,22 @@ def main():
     do_bwd = not args.fwd_only
 
     def step(ev=None):
+        # Events on torch's current stream, which is the stream the library launches on.
         if ev:
             ev[0].record()
         fa.fwd(q, k, v, causal=True, out=o, lse=lse)
         if ev:
             ev[1].record()
         if do_bwd:
-            fa.bwd(q, k, v, o, lse, do, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
-            if ev:
-                ev[2].record()
+            for i, stage in enumerate((1, 2, 4)):
+                fa.bwd_stages(q, k, v, o, lse, do, ws, dq, dk, dv, stage_mask=stage, causal=True)
+                if ev:
+                    ev[2 + i].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -146,7 +148,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if do_bwd else 0.0
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[4]) for e in evs])) if do_bwd else 0.0
+    bwd_main_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) if do_bwd else 0.0
+    bwd_pre_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if do_bwd else 0.0
+    bwd_fin_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs])) if do_bwd else 0.0
     ms_per_step = wall * 1e3 / args.steps
 
     f_fwd = attention_flops(B, H, N, d, True)
@@ -154,8 +159,10 @@ def main():
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
 
     # Roofline of the dominant kernel: algorithmic FLOPs per launch / its event-timed duration.
-    if do_bwd and bwd_ms > fwd_ms:
-        dom, dom_ms, dom_flops, files = "attn_bwd", bwd_ms, f_bwd, ["fa_bwd.hip", "fa_device.h"]
+    # All five products of the backward run in its main kernel (the other two
+    # launches are O(N d) streaming passes).
+    if do_bwd and bwd_main_ms > fwd_ms:
+        dom, dom_ms, dom_flops, files = "attn_bwd_main", bwd_main_ms, f_bwd, ["fa_bwd.hip", "fa_device.h"]
     else:
         dom, dom_ms, dom_flops, files = "attn_fwd", fwd_ms, f_fwd, ["fa_fwd.hip", "fa_device.h"]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
@@ -181,6 +188,8 @@ def main():
                    "B": B, "H": H, "N": N, "d": d, "causal": True},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "breakdown": {"fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                      "bwd_pre_ms": round(bwd_pre_ms, 4), "bwd_main_ms": round(bwd_main_ms, 4),
+                      "bwd_finish_ms": round(bwd_fin_ms, 4),
                       "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
                       "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if do_bwd else None},
         "roofline": roofline,

@@ -27,6 +27,8 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "fa_bwd": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
                         _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
+    "fa_bwd_stages": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
+                               _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _p]),
     "fa_bwd_f32": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
     "fa_quant_fp8": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),

@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "quant_fp8", "fwd_fp8"]
+__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "quant_fp8", "fwd_fp8"]
 
 
 def _stream(t: torch.Tensor):
@@ -96,6 +96,22 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
             B, H, N, d, float(scale), int(bool(causal)), _stream(q))
     _lib.check(st, "fa_bwd" if dt == torch.bfloat16 else "fa_bwd_f32")
     return dq, dk, dv
+
+
+def bwd_stages(q, k, v, o, lse, do, workspace, dq, dk, dv, stage_mask: int, causal: bool = False,
+               scale: float | None = None):
+    """Run selected stages of the bf16 backward (1 preprocess, 2 main, 4 finish) into given buffers."""
+    B, H, N, d = _shape4(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_tensor(t, n, torch.bfloat16, (B, H, N, d))
+    _check_tensor(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _lib.load().fa_bwd_stages(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   B, H, N, d, float(scale), int(bool(causal)), int(stage_mask), _stream(q))
+    _lib.check(st, "fa_bwd_stages")
 
 
 def quant_fp8(x, rot=None, block_rows: int = 64, x8=None, scales=None):

@@ -96,7 +96,8 @@ int fwd_common(fa::DType dt, const void* q, const void* k, const void* v, void* 
 
 int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, int B, int H, int N,
-               int d, float scale, int causal, void* stream) {
+               int d, float scale, int causal, void* stream, int stage_mask = 7) {
+  if (stage_mask < 1 || stage_mask > 7) return fail(FA_ERR_INVALID, "stage_mask must be in 1..7 (got %d)", stage_mask);
   int rc = check_shape(B, H, N, d, scale);
   if (rc) return rc;
   const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
@@ -114,7 +115,7 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   const size_t acc_bytes = align256((size_t)B * H * N * d * 4);
   fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)ws, (float*)((char*)ws + acc_bytes),
                 N, 0, scale, log2e_scale(scale), 0};
-  return launched(fa::launch_bwd(dt, d, causal, a, B, H, (hipStream_t)stream), "attention backward");
+  return launched(fa::launch_bwd(dt, d, causal, a, B, H, stage_mask, (hipStream_t)stream), "attention backward");
 }
 
 }  // namespace
@@ -153,6 +154,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            float scale, int causal, void* stream) {
   return bwd_common(fa::DType::BF16, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                     scale, causal, stream);
+}
+
+int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                  float scale, int causal, int stage_mask, void* stream) {
+  return bwd_common(fa::DType::BF16, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                    scale, causal, stream, stage_mask);
 }
 
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,

@@ -89,8 +89,8 @@ struct TrF32 {
   __device__ static __forceinline__ Frag pack(const float* x) { return x[0]; }
 };
 
-// Store NB bytes (4, 8, 16 or 32; destination aligned to min(NB, 16)) from
-// an array of elements.
+// Store NB bytes (4, 8, 16, 32 or 64; destination aligned to min(NB, 16))
+// from an array of elements.
 template <int NB>
 __device__ __forceinline__ void store_bytes(void* dst, const void* src) {
   if constexpr (NB == 4) {
@@ -100,9 +100,9 @@ __device__ __forceinline__ void store_bytes(void* dst, const void* src) {
   } else if constexpr (NB == 16) {
     *(u32x4*)dst = *(const u32x4*)src;
   } else {
-    static_assert(NB == 32, "unsupported store width");
-    ((u32x4*)dst)[0] = ((const u32x4*)src)[0];
-    ((u32x4*)dst)[1] = ((const u32x4*)src)[1];
+    static_assert(NB == 32 || NB == 64, "unsupported store width");
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) ((u32x4*)dst)[i] = ((const u32x4*)src)[i];
   }
 }
 

@@ -93,6 +93,22 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
            void* workspace, size_t workspace_bytes,
            int B, int H, int N, int d, float scale, int causal, void* stream);
 
+/* The stages of fa_bwd, for callers that schedule them themselves (and for
+ * timing the main stage alone). fa_bwd runs stage_mask 7 = 1 | 2 | 4:
+ *   1  preprocess: D = rowsum(dO * O) and a zeroed float32 dQ accumulator,
+ *      both in the workspace;
+ *   2  main: the recompute of P and the five products; writes dk and dv and
+ *      adds into the dQ accumulator;
+ *   4  finish: dq = scale * accumulator, cast to bf16.
+ * Bits are run in the order 1, 2, 4. Each stage reads what the earlier
+ * stages left in the workspace, so stages of one problem must run in order
+ * on one stream with the workspace untouched in between. Same arguments and
+ * checks as fa_bwd (bf16); stage_mask outside 1..7 gives FA_ERR_INVALID. */
+FA_API int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int H, int N, int d, float scale, int causal, int stage_mask, void* stream);
+
 /* Backward, float32 tensors. Same contract as fa_bwd. */
 FA_API int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
                const float* dout, float* dq, float* dk, float* dv,
