@@ -92,6 +92,9 @@ def main():
     ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before the warm-up, copy MIB MiB device-to-device once (a transfer of known "
+                         "size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -123,6 +126,14 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), device=dev, dtype=torch.uint8)
     do_bwd = not args.fwd_only
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, device=dev, dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         # Events on torch's current stream, which is the stream the library launches on.

@@ -1,4 +1,5 @@
-// Fused exact-attention forward for gfx950 (bf16 and float32 inputs).
+// Fused exact-attention forward for gfx950: float32 inputs (this file) and the
+// bf16 entry (fa_fwd_bf16.hip).
 //
 // What it computes ("FlashAttention v1～v4 完整进化史", v1 pseudocode and v2
 // part 1; "6.1 FlashAttention V1详解", section 5.1): for one query tile the
@@ -259,13 +260,11 @@ hipError_t dispatch(int d, int causal, const FwdArgs& a, int grid, hipStream_t s
 
 }  // namespace
 
-int fwd_query_tile() { return kBR; }
-
 hipError_t launch_fwd(DType dt, int d, int causal, FwdArgs a, int B, int H, hipStream_t s) {
+  if (dt == DType::BF16) return launch_fwd_bf16(d, causal, a, B, H, s);
   a.n_qtiles = (a.N + kBR - 1) / kBR;
   const long long grid = (long long)B * H * a.n_qtiles;
   a.remap = (grid % 8 == 0) ? 1 : 0;
-  if (dt == DType::BF16) return dispatch<TrBF16, 2>(d, causal, a, (int)grid, s);
   return dispatch<TrF32, 1>(d, causal, a, (int)grid, s);
 }
 
