@@ -1,4 +1,6 @@
-// Recompute-based attention backward for gfx950 (bf16 and float32).
+// Recompute-based attention backward for gfx950: the preprocess and finish
+// passes (both types) and the float32 main kernel; the bf16 main kernel is in
+// fa_bwd_bf16.hip.
 //
 // What it computes ("6.1 FlashAttention V1详解", sections 6.1-6.2;
 // "FlashAttention v1～v4 完整进化史", v2 part 1 and v4 part 4): S and P are
@@ -356,11 +358,16 @@ hipError_t run(int causal, BwdArgs a, int B, int H, int stage_mask, hipStream_t 
     if (e != hipSuccess) return e;
   }
   if (stage_mask & 2) {
+    if constexpr (sizeof(typename Tr::T) == 2) {
+      hipError_t e = launch_bwd_bf16_main(D, causal, a, B, H, s);
+      if (e != hipSuccess) return e;
+    } else {
     a.n_tiles = (a.N + kBC - 1) / kBC;
     const long long grid = (long long)B * H * a.n_tiles;
     a.remap = grid % 8 == 0 ? 1 : 0;
     hipError_t e = causal ? launch_main<Tr, D, true>(a, (int)grid, s) : launch_main<Tr, D, false>(a, (int)grid, s);
     if (e != hipSuccess) return e;
+    }
   }
   if (stage_mask & 4) {
     const long long n4 = rows * D / 4;

@@ -52,7 +52,7 @@ struct Cfg {
   static constexpr int CPR = RB / 16;               // 16-byte chunks per row
   static constexpr int TILE = kBC * RB;             // bytes of one K or V tile
   static constexpr int STAGE = 2 * TILE;
-  static constexpr int LDS_BYTES = kStages * STAGE;
+  static constexpr int LDS_BYTES = kStages * STAGE;   // three __shared__ stages
   static constexpr int LPW = TILE / 1024 / kWaves;  // 1 KiB wave-loads per wave per tensor
   static constexpr int RPL = 1024 / RB;             // rows per wave-load
   static constexpr int KSTEPS = D / 16;
@@ -69,26 +69,9 @@ __device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >
 template <int D>
 __device__ __forceinline__ int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-// Transposed 64-bit LDS read (see the V fragment layout below). Issued as
-// inline assembly: the intrinsic form makes the compiler wait for every
-// outstanding HBM->LDS tile load before each read, which would drain the
-// prefetch ring. The results are made available by tr_wait().
-template <int OFF>
-__device__ __forceinline__ u32x2 tr_read(unsigned lds_addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF) : "memory");
-  return r;
-}
-// Wait for every outstanding LDS read; the values read are passed through so
-// their users cannot be scheduled before the wait.
-template <int N>
-__device__ __forceinline__ void tr_wait(u32x2 (&v)[N]) {
-  static_assert(N == 8 || N == 4, "tr_wait arity");
-  if constexpr (N == 8)
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
-  else
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+// Transposed 64-bit LDS read (see the V fragment layout below).
+__device__ __forceinline__ u32x2 tr_read(const unsigned char* lds_byte_ptr) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, lds_byte_ptr)));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
@@ -102,7 +85,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // capture buffer resources.
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
+  // One variable per ring stage: with the stage known at compile time the
+  // compiler can tell a tile being read from the tile being loaded, and needs
+  // no wait on the in-flight loads before the reads.
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[C::STAGE];
+  auto sp = [&](auto stag) -> unsigned char* {
+    constexpr int S = decltype(stag)::value;
+    if constexpr (S == 0) return st0;
+    else if constexpr (S == 1) return st1;
+    else return st2;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -131,14 +125,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // --- tile loads: HBM -> LDS, no registers. Wave-load t covers rows
   // [t*RPL, t*RPL+RPL) of the tile; lane l fills physical chunk l % CPR of
   // row t*RPL + l / CPR with the logical chunk that the swizzle maps there.
-  auto issue_tile = [&](int j, int stage) __device__ {
+  auto issue_tile = [&](int j, auto stag) __device__ {
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int tl = wave * C::LPW + i;
       const int row = tl * C::RPL + lane / C::CPR;
       const int p = lane % C::CPR;
       const unsigned grow = (unsigned)(j * kBC + row) * C::RB;
-      unsigned char* kd = smem + stage * C::STAGE + tl * 1024;
+      unsigned char* kd = sp(stag) + tl * 1024;
       unsigned char* vd = kd + C::TILE;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS(void, kd), 16, grow + 16 * (p ^ k_swz<D>(row)), 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS(void, vd), 16, grow + 16 * (p ^ v_swz<D>(row)), 0, 0, 0);
@@ -169,7 +163,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // address serves every block through an XOR.
   const int g16 = lane >> 4, j16 = lane & 15;
   const int vs = j16 >> 2, vq = j16 & 3;
-  const unsigned lds_base = (unsigned)(size_t)LDS(unsigned char, smem);
   const unsigned v_lane = (unsigned)(vs + 8 * hh) * C::RB + 16 * ((2 * (g16 & 1) + (vq >> 1)) ^ v_swz<D>(vs)) +
                           8 * (vq & 1);
 
@@ -180,14 +173,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < C::DBLK; ++i) oacc[i] = f32x16{};
 
-  // S^T of one 32-key block (blk) of the tile in `stage`.
-  auto qk = [&](int stage, int blk, f32x16& s) __device__ {
-    const unsigned kb = (unsigned)stage * C::STAGE + k_lane;
+  // S^T of one 32-key block (blk) of the tile in stage `stag`.
+  auto qk = [&](auto stag, int blk, f32x16& s) __device__ {
+    const unsigned char* kt = sp(stag);
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      const unsigned addr = (kb ^ (32u * kk)) + blk * 32 * C::RB;
-      const bf16x8 af = *LDS(bf16x8, smem + addr);
+      const unsigned addr = (k_lane ^ (32u * kk)) + blk * 32 * C::RB;
+      const bf16x8 af = *LDS(bf16x8, kt + addr);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], acc, 0, 0, 0);
     }
     s = acc;
@@ -196,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // Softmax of one 32-key block against the reference maximum, then
   // O += V^T P^T over its 32 keys. MASK applies key < N and the causal
   // condition (diagonal and ragged blocks only).
-  auto softmax_pv = [&](auto mask_tag, int u, f32x16& s, int stage, int blk) __device__ {
+  auto softmax_pv = [&](auto mask_tag, int u, f32x16& s, auto stag, int blk) __device__ {
     constexpr bool MASK = decltype(mask_tag)::value;
     if constexpr (MASK) {
       const int key0 = u * 32;
@@ -232,19 +225,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     l += (part[0] + part[1]) + (part[2] + part[3]);
     // V tile of `stage`, 16-key half ks of block blk: the key offset is a
     // compile-time immediate once blk and ks are.
-    const unsigned vb = lds_base + (unsigned)stage * C::STAGE + C::TILE + v_lane;
-    unsigned vaddr[C::DBLK];
-#pragma unroll
-    for (int db = 0; db < C::DBLK; ++db) vaddr[db] = vb ^ (64u * db);
+    const unsigned char* vt = sp(stag) + C::TILE;
     auto pv_half = [&](auto ofs_tag, int ks) __device__ {
       constexpr int OFS = decltype(ofs_tag)::value;
       u32x2 v[2 * C::DBLK];
 #pragma unroll
       for (int db = 0; db < C::DBLK; ++db) {
-        v[2 * db] = tr_read<OFS>(vaddr[db]);
-        v[2 * db + 1] = tr_read<OFS + 4 * C::RB>(vaddr[db]);
+        const unsigned char* vp = vt + (v_lane ^ (64u * db)) + OFS;
+        v[2 * db] = tr_read(vp);
+        v[2 * db + 1] = tr_read(vp + 4 * C::RB);
       }
-      tr_wait(v);
 #pragma unroll
       for (int db = 0; db < C::DBLK; ++db) {
         const u32x4 w = {v[2 * db][0], v[2 * db][1], v[2 * db + 1][0], v[2 * db + 1][1]};
@@ -267,28 +257,35 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int u_end = CAUSAL ? min(n_blk, (min(q0 + kBR, N) - 1) / 32 + 1) : n_blk;
   auto active = [&](int u) __device__ { return u < u_end && (!CAUSAL || u * 32 <= wrow0 + 31); };
   auto masked = [&](int u) __device__ { return u * 32 + 32 > N || (CAUSAL && u * 32 + 31 > wrow0); };
-  auto block = [&](int u, f32x16& cur, f32x16& nxt, int stage, int blk, int nstage, int nblk) __device__ {
-    if (active(u + 1)) qk(nstage, nblk, nxt);
+  auto block = [&](int u, f32x16& cur, f32x16& nxt, auto stag, int blk, auto nstag, int nblk) __device__ {
+    if (active(u + 1)) qk(nstag, nblk, nxt);
     if (active(u)) {
       if (masked(u))
-        softmax_pv(std::true_type{}, u, cur, stage, blk);
+        softmax_pv(std::true_type{}, u, cur, stag, blk);
       else
-        softmax_pv(std::false_type{}, u, cur, stage, blk);
+        softmax_pv(std::false_type{}, u, cur, stag, blk);
     }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
 
   // Prologue: tiles 0 and 1 in flight, S of block 0.
-  issue_tile(0, 0);
-  if (kv_end > 1) issue_tile(1, 1);
+  issue_tile(0, I0{});
+  if (kv_end > 1) issue_tile(1, I1{});
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   f32x16 sa, sb;
-  qk(0, 0, sa);
+  qk(I0{}, 0, sa);
 
-  // Tile j: blocks 2j (S in sa) and 2j+1; the next block's QK^T is issued
-  // alongside each softmax. The barrier makes tile j+1 resident and frees the
-  // stage of tile j-1 for tile j+2.
-  for (int j = 0; j < kv_end; ++j) {
+  // Tile j (in stage j % 3): blocks 2j (S in sa) and 2j+1; the next block's
+  // QK^T is issued alongside each softmax. The barrier makes tile j+1
+  // resident and frees the stage of tile j-1 for tile j+2. The loop is
+  // unrolled by the ring depth so every stage is a compile-time variable.
+  auto tile = [&](int j, auto stag) __device__ {
+    constexpr int S = decltype(stag)::value;
+    using S1 = std::integral_constant<int, (S + 1) % kStages>;
+    using S2 = std::integral_constant<int, (S + 2) % kStages>;
     if (j > 0) {
       // The compiler does not order LDS-destination loads before a barrier by
       // itself: wait for this wave's loads of tile j+1 (the only ones in
@@ -296,11 +293,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
     }
-    if (j + 2 < kv_end) issue_tile(j + 2, (j + 2) % kStages);
-    const int st = j % kStages, st1 = (j + 1) % kStages;
-    block(2 * j, sa, sb, st, 0, st, 1);
-    block(2 * j + 1, sb, sa, st, 1, st1, 0);
+    if (j + 2 < kv_end) issue_tile(j + 2, S2{});
+    block(2 * j, sa, sb, stag, 0, stag, 1);
+    block(2 * j + 1, sb, sa, stag, 1, S1{}, 0);
+  };
+  int j = 0;
+  for (; j + kStages <= kv_end; j += kStages) {
+    tile(j, I0{});
+    tile(j + 1, I1{});
+    tile(j + 2, I2{});
   }
+  if (j < kv_end) tile(j, I0{});
+  if (j + 1 < kv_end) tile(j + 1, I1{});
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) ln 2 in natural-log units.
   const float lt = halves_sum(l);

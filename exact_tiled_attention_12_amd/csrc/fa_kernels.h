@@ -67,6 +67,7 @@ hipError_t launch_fwd(DType dt, int d, int causal, FwdArgs a, int B, int H, hipS
 hipError_t launch_fwd_bf16(int d, int causal, FwdArgs a, int B, int H, hipStream_t s);
 // stage_mask: 1 = preprocess (D, zero the dQ accumulator), 2 = main, 4 = dQ finish.
 hipError_t launch_bwd(DType dt, int d, int causal, BwdArgs a, int B, int H, int stage_mask, hipStream_t s);
+hipError_t launch_bwd_bf16_main(int d, int causal, BwdArgs a, int B, int H, hipStream_t s);
 hipError_t launch_quant_fp8(int d, QuantArgs a, int B, int H, hipStream_t s);
 hipError_t launch_fwd_fp8(int d, int causal, Fp8FwdArgs a, int B, int H, hipStream_t s);
 
