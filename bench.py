@@ -173,9 +173,9 @@ def main():
     # All five products of the backward run in its main kernel (the other two
     # launches are O(N d) streaming passes).
     if do_bwd and bwd_main_ms > fwd_ms:
-        dom, dom_ms, dom_flops, files = "attn_bwd_main", bwd_main_ms, f_bwd, ["fa_bwd.hip", "fa_device.h"]
+        dom, dom_ms, dom_flops, files = "attn_bwd_main", bwd_main_ms, f_bwd, ["fa_bwd_bf16.hip", "fa_device.h"]
     else:
-        dom, dom_ms, dom_flops, files = "attn_fwd", fwd_ms, f_fwd, ["fa_fwd.hip", "fa_device.h"]
+        dom, dom_ms, dom_flops, files = "attn_fwd", fwd_ms, f_fwd, ["fa_fwd_bf16.hip", "fa_device.h"]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
