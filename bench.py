@@ -98,7 +98,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the attention of each (batch, head) is independent; see the sharding notes in DESIGN.md)",
+              "(the attention of each (batch, head) is independent, so heads would shard across GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
