@@ -143,6 +143,8 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = 
         scale = 1.0 / math.sqrt(d)
     out = torch.empty((B, H, N, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
     lse = torch.empty((B, H, N), device=q8.device, dtype=torch.float32) if lse is None else lse
+    _check_tensor(out, "out", torch.bfloat16, (B, H, N, d))
+    _check_tensor(lse, "lse", torch.float32, (B, H, N))
     st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), sq.data_ptr(), sk.data_ptr(),
                                 sv.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
                                 int(bool(causal)), _stream(q8))

@@ -47,6 +47,10 @@ int check_shape(int B, int H, int N, int d, float scale) {
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d must be 64 or 128 (got %d)", d);
   if (!std::isfinite(scale) || scale < 0.f)
     return fail(FA_ERR_UNSUPPORTED, "scale must be finite and >= 0 (got %g)", (double)scale);
+  // Kernels address one (batch, head) with 32-bit byte offsets.
+  if ((long long)N * d * 4 > (1LL << 30))
+    return fail(FA_ERR_UNSUPPORTED, "sequence too long: N * d = %lld exceeds 2^28 elements per head",
+                (long long)N * d);
   const long long tiles = (long long)B * H * ((N + 63) / 64);
   if (tiles > INT_MAX / 2 || (long long)B * H * N > INT_MAX)
     return fail(FA_ERR_UNSUPPORTED, "problem too large: B*H*N = %lld exceeds the supported range",

@@ -1,7 +1,504 @@
-// fp8 quantisation and forward for gfx950 (placeholder until the kernels land).
+// fp8 (e4m3) path for gfx950: block quantisation with an optional orthogonal
+// rotation, and the fused attention forward on fp8 operands.
+//
+// What it computes ("FlashAttention v1～v4 完整进化史", v3 part 3):
+//   * each block of 64 rows (all d columns) of one (batch, head) gets its own
+//     scale s = amax / 448 instead of one scale for the whole tensor; Q and K
+//     may first be multiplied by one orthogonal matrix, which leaves Q K^T
+//     unchanged and spreads outlier channels over all columns;
+//   * both attention products run on fp8 matrix cores; the exponentiated
+//     scores are themselves rounded to fp8 for the product with V.
+// Format: OCP e4m3fn (bias 7, largest finite 448, no infinity); encoding
+// saturates to +-448 and then rounds to nearest, ties to even.
+//
+// Attention schedule (same skeleton as the bf16 forward):
+//   * one workgroup = 8 waves = 256 query rows; each wave owns 32 rows, which
+//     lie inside one 64-row scale block; key tiles of 64 keys coincide with
+//     the scale blocks of K and V;
+//   * K and V tiles move from HBM into a 3-stage LDS ring with buffer loads
+//     that write LDS directly, two tiles ahead of use;
+//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x64_f8f6f4. K rows are
+//     read in a permuted order so that each lane's 32 scores of its query are
+//     exactly the 32 bytes of the P^T operand; V stays row-major and is read
+//     with ds_read_b64_tr_b8;
+//   * the scores are scaled by scale * log2(e) * sQ * sK_j in one FMA that
+//     also folds in the factor 448, so P' = 448 P~ comes out of exp2 ready to
+//     convert; l sums the float32 P' (the factor 448 cancels in O = acc / l);
+//   * the V block scale differs per tile, so the accumulator is kept in units
+//     of the current tile's scale: before tile j's product it is multiplied by
+//     alpha_j * sV_{j-1} / sV_j, and O = acc * sV_last / l at the end.
+#include <type_traits>
+
+#include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
-hipError_t launch_quant_fp8(int, QuantArgs, int, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_fwd_fp8(int, int, Fp8FwdArgs, int, int, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+// ---------------------------------------------------------------- encoder
+
+// e4m3fn code of x: saturate to +-448, round to nearest even, NaN -> 0x7F.
+// Works on the float32 bit pattern: for normal results the 3 kept mantissa
+// bits are rounded at bit 20 (the exponent carry is the correct result), and
+// results below 2^-6 are multiples of 2^-9, rounded with rint.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x7F800000u) {
+    code = 0x7Fu;
+  } else if (a >= 0x43E00000u) {            // |x| >= 448
+    code = 0x7Eu;
+  } else if (a >= 0x3C800000u) {            // |x| >= 2^-6: normal e4m3
+    code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  } else {
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.f);
+  }
+  return sign | code;
+}
+
+// ---------------------------------------------------------------- quantiser
+
+constexpr int kQRows = 64;      // rows per scale block
+constexpr int kQThreads = 256;
+
+enum QuantMode { kBlockScale = 0, kAmaxOnly = 1, kGivenScale = 2 };
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// One workgroup per 64-row block of one (batch, head). Thread t owns rows
+// 8*(t/32) .. +8 and columns CPT*(t%32) .. +CPT of the block.
+template <int D, bool ROT, int MODE>
+__global__ __launch_bounds__(kQThreads) void quant_kernel(QuantArgs a, int nb) {
+  constexpr int CPT = D / 32;
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x % nb;
+  const int bh = blockIdx.x / nb;
+  const int N = a.N;
+  const int r0 = blk * kQRows;
+  const int rows = min(kQRows, N - r0);
+  const size_t off = ((size_t)bh * N + r0) * D;
+  const __bf16* x = (const __bf16*)a.x + off;
+  const int cg = tid & 31, rg = tid >> 5;
+
+  float y[8][CPT];
+  if constexpr (ROT) {
+    __shared__ float xs[kQRows][D];
+    __shared__ float rs[D][D];
+    for (int i = tid; i < D * D / 4; i += kQThreads) ((f32x4*)&rs[0][0])[i] = ((const f32x4*)a.rot)[i];
+    for (int i = tid; i < kQRows * D / 4; i += kQThreads) {
+      const int r = i / (D / 4), c4 = i % (D / 4);
+      bf16x4 v = {};
+      if (r < rows) v = *(const bf16x4*)(x + (size_t)r * D + 4 * c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[r][4 * c4 + e] = (float)v[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) y[i][c] = 0.f;
+    // y = x * rot in float32, summed over k in increasing order.
+    for (int k = 0; k < D; ++k) {
+      float rv[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) rv[c] = rs[k][CPT * cg + c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xv = xs[8 * rg + i][k];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) y[i][c] = __builtin_fmaf(xv, rv[c], y[i][c]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * rg + i;
+      if (r < rows) {
+        const __bf16* p = x + (size_t)r * D + CPT * cg;
+        if constexpr (CPT == 4) {
+          const bf16x4 v = *(const bf16x4*)p;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) y[i][c] = (float)v[c];
+        } else {
+          const bf16x2v v = *(const bf16x2v*)p;
+          y[i][0] = (float)v[0];
+          y[i][1] = (float)v[1];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) y[i][c] = 0.f;
+      }
+    }
+  }
+
+  float s;
+  float* sc = a.scales + (size_t)bh * nb + blk;
+  if constexpr (MODE == kGivenScale) {
+    s = *sc;
+  } else {
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) am = fmaxf(am, fabsf(y[i][c]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+    __shared__ float red[kQThreads / 64];
+    if ((tid & 63) == 0) red[tid >> 6] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if constexpr (MODE == kAmaxOnly) {
+      if (tid == 0) *sc = am;
+      return;
+    }
+    s = am == 0.f ? 1.f : am / 448.f;   // correctly rounded float32 division
+    if (tid == 0) *sc = s;
+  }
+
+  unsigned char* x8 = a.x8 + off;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * rg + i;
+    if (r >= rows) continue;
+    uint32_t w = 0;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) w |= e4m3_code(y[i][c] / s) << (8 * c);
+    if constexpr (CPT == 4)
+      *(uint32_t*)(x8 + (size_t)r * D + 4 * cg) = w;
+    else
+      *(uint16_t*)(x8 + (size_t)r * D + 2 * cg) = (uint16_t)w;
+  }
+}
+
+// Per-tensor scale: the largest of the per-block amax values written by the
+// kAmaxOnly pass, turned into s and broadcast to every block entry.
+constexpr int kRedThreads = 1024;
+__global__ __launch_bounds__(kRedThreads) void quant_tensor_scale_kernel(float* scales, int n) {
+  const int tid = threadIdx.x;
+  float am = 0.f;
+  for (int i = tid; i < n; i += kRedThreads) am = fmaxf(am, scales[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+  __shared__ float red[kRedThreads / 64];
+  if ((tid & 63) == 0) red[tid >> 6] = am;
+  __syncthreads();
+  am = red[0];
+#pragma unroll
+  for (int i = 1; i < kRedThreads / 64; ++i) am = fmaxf(am, red[i]);
+  const float s = am == 0.f ? 1.f : am / 448.f;
+  for (int i = tid; i < n; i += kRedThreads) scales[i] = s;
+}
+
+template <int D, bool ROT>
+hipError_t launch_quant_d(const QuantArgs& a, int B, int H, hipStream_t st) {
+  const int nb = (a.N + kQRows - 1) / kQRows;
+  const int grid = B * H * nb;
+  if (a.block_rows == 64) {
+    hipLaunchKernelGGL((quant_kernel<D, ROT, kBlockScale>), dim3(grid), dim3(kQThreads), 0, st, a, nb);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((quant_kernel<D, ROT, kAmaxOnly>), dim3(grid), dim3(kQThreads), 0, st, a, nb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quant_tensor_scale_kernel, dim3(1), dim3(kRedThreads), 0, st, a.scales, grid);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((quant_kernel<D, ROT, kGivenScale>), dim3(grid), dim3(kQThreads), 0, st, a, nb);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- attention
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBR = 32 * kWaves;    // query rows per workgroup
+constexpr int kBC = 64;             // keys per tile = rows per scale block
+constexpr int kStages = 3;
+constexpr int kD = 128;
+constexpr int kRB = kD;             // bytes per fp8 row
+constexpr int kTile = kBC * kRB;    // 8 KiB
+constexpr int kStage = 2 * kTile;   // K then V
+constexpr float kLog2_448 = 8.807354922057604f;
+
+#define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r).
+// K: the 16 rows one 16-lane group reads together (keys 0-7 and 16-23 of a
+// 32-key block, shifted by 4 per group) land on 16 distinct bank groups.
+// V: the 8 consecutive rows x 2 chunks of one transposed read do.
+__device__ __forceinline__ int k_swz(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
+__device__ __forceinline__ int v_swz(int r) { return r & 6; }
+
+__device__ __forceinline__ u32x2 tr8_read(const unsigned char* lds_byte_ptr) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, lds_byte_ptr)));
+}
+
+__device__ __forceinline__ f32x16 mma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // Format 0 (e4m3) for both operands; zero block scales select the plain
+  // (unscaled) instruction.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Accumulator slot r of lane half h in 32-key block t holds key 32t + 16h + r
+// of the tile (the K rows are permuted to make it so). A position p of the A
+// operand therefore loads key 32t + 16*((p>>2)&1) + 4*(p>>3) + (p&3).
+__device__ __forceinline__ int pos_to_key(int p) { return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3); }
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[kStage];
+  auto sp = [&](auto stag) -> unsigned char* {
+    constexpr int S = decltype(stag)::value;
+    if constexpr (S == 0) return st0;
+    else if constexpr (S == 1) return st1;
+    else return st2;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  int wg = blockIdx.x;
+  if (a.remap) wg = xcd_remap(wg, gridDim.x);
+  const int bh = wg / a.n_qtiles;
+  const int t = wg - bh * a.n_qtiles;
+  const int qt = CAUSAL ? (a.n_qtiles - 1 - t) : t;
+  const int N = a.N;
+  const int nb = (N + kBC - 1) / kBC;
+  const size_t base = (size_t)bh * (size_t)N * kD;
+  const unsigned head_bytes = (unsigned)N * kRB;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q8 + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k8 + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v8 + base, head_bytes);
+  const float* sk = a.sk + (size_t)bh * nb;
+  const float* sv = a.sv + (size_t)bh * nb;
+
+  const int q0 = qt * kBR;
+  const int wrow0 = q0 + wave * 32;
+  const int qrow = wrow0 + l32;
+  const float sq = a.sq[(size_t)bh * nb + min(wrow0 / kBC, nb - 1)];
+  const float cq = a.c * sq;
+
+  const int kv_end = CAUSAL ? min(nb, (min(q0 + kBR, N) - 1) / kBC + 1) : nb;
+
+  // Tile loads: wave w fills rows 8w .. 8w+7 of K and of V; lane l writes
+  // physical chunk l % 8 of row 8w + l / 8 with the logical chunk the
+  // swizzle maps there.
+  auto issue_tile = [&](int j, auto stag) __device__ {
+    const int row = wave * 8 + (lane >> 3);
+    const int p = lane & 7;
+    const unsigned grow = (unsigned)(j * kBC + row) * kRB;
+    unsigned char* kd = sp(stag) + wave * 1024;
+    unsigned char* vd = kd + kTile;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS(void, kd), 16, grow + 16 * (p ^ k_swz(row)), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS(void, vd), 16, grow + 16 * (p ^ v_swz(row)), 0, 0, 0);
+  };
+
+  // Q rows of this wave as the B operand of S^T = K Q^T: lane (l32, hh)
+  // holds bytes 64*ks + 32*hh .. +32 of row qrow for d step ks.
+  i32x8 qf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const unsigned o = (unsigned)qrow * kRB + 64 * ks + 32 * hh;
+    const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0));
+    const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, o + 16, 0, 0));
+    qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // K fragment of lane (l32, hh) for 32-key block t, d step ks, 16-byte half
+  // hb: row 32t + pos_to_key(l32), logical chunk 4ks + 2hh + hb. The swizzle
+  // depends on l32 only, and ks / hb flip address bits 6 / 4.
+  const int krow = pos_to_key(l32);
+  const unsigned k_lane = (unsigned)krow * kRB + 16 * ((2 * hh) ^ k_swz(krow));
+  // V fragment for d block mt, read q (keys 32(q/2) + 16h + 8(q%2) + 0..7):
+  // source lane j of 16-lane group G points at row 16(G/2) + j/2 (plus the
+  // read's offset) and bytes 32mt + 16(G%2) + 8(j%2); the result lane then
+  // holds 8 consecutive keys of one d column.
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int vrow = 16 * (g16 >> 1) + (j16 >> 1);
+  const unsigned v_lane = (unsigned)vrow * kRB + 16 * ((g16 & 1) ^ v_swz(vrow)) + 8 * (j16 & 1);
+
+  float m = -INFINITY;     // running maximum of this lane's row (scaled log2 units)
+  float l = 0.f;           // sum of P' = 448 P~ over this lane half's keys
+  float sv_cur = 1.f;      // V scale the accumulator is expressed in
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
+
+  auto qk = [&](auto stag, f32x16 (&s)[2]) __device__ {
+    const unsigned char* kt = sp(stag);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const unsigned a0 = (k_lane ^ (64u * ks)) + tb * 32 * kRB;
+        const u32x4 lo = *LDS(u32x4, kt + a0);
+        const u32x4 hi = *LDS(u32x4, kt + (a0 ^ 16u));
+        const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        acc = mma_fp8(kf, qf[ks], acc);
+      }
+      s[tb] = acc;
+    }
+  };
+
+  // Softmax of tile j (scores in s) and O^T += V^T P^T over its 64 keys.
+  // Masking (keys >= N, causal) is applied on ragged and diagonal tiles only.
+  auto softmax_pv = [&](int j, bool mask, f32x16 (&s)[2], auto stag) __device__ {
+    const float cj = cq * sk[j];
+    const float svj = sv[j];
+    if (mask) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * kBC + 32 * tb + 16 * hh + r;
+          const bool ok = key < N && (!CAUSAL || key <= qrow);
+          s[tb][r] = ok ? s[tb][r] * cj : -INFINITY;
+        }
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) s[tb] *= cj;
+    }
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    const float gamma = alpha * (sv_cur / svj);
+    m = m_new;
+    sv_cur = svj;
+    l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) oacc[mt] *= gamma;
+    // P' = 2^(s - m + log2 448) = 448 P~, converted two values at a time.
+    const float mo = m_use - kLog2_448;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    i32x8 pf;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[i] = fast_exp2(s[w >> 2][4 * (w & 3) + i] - mo);
+        part[i] += e[i];
+      }
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], word, true);
+      pf[w] = word;
+    }
+    l += (part[0] + part[1]) + (part[2] + part[3]);
+    const unsigned char* vt = sp(stag) + kTile;
+    u32x2 vr[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vr[mt][q] = tr8_read(vt + (v_lane ^ (32u * mt)) + 4096 * (q >> 1) + 1024 * (q & 1));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const i32x8 vf = {(int)vr[mt][0][0], (int)vr[mt][0][1], (int)vr[mt][1][0], (int)vr[mt][1][1],
+                        (int)vr[mt][2][0], (int)vr[mt][2][1], (int)vr[mt][3][0], (int)vr[mt][3][1]};
+      oacc[mt] = mma_fp8(vf, pf, oacc[mt]);
+    }
+  };
+
+  // A wave computes tile j only if some of its rows see a key of it.
+  auto active = [&](int j) __device__ { return j < kv_end && (!CAUSAL || j * kBC <= wrow0 + 31); };
+  auto masked = [&](int j) __device__ { return j * kBC + kBC > N || (CAUSAL && j * kBC + kBC - 1 > wrow0); };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+
+  issue_tile(0, I0{});
+  if (kv_end > 1) issue_tile(1, I1{});
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  f32x16 sc[2], sn[2];
+  if (active(0)) qk(I0{}, sc);
+
+  // Tile j in stage j % 3. The barrier makes tile j+1 resident and frees
+  // the stage of tile j-1 for tile j+2; S of tile j+1 is formed while the
+  // softmax of tile j runs.
+  auto tile = [&](int j, auto stag) __device__ {
+    constexpr int S = decltype(stag)::value;
+    using S1 = std::integral_constant<int, (S + 1) % kStages>;
+    using S2 = std::integral_constant<int, (S + 2) % kStages>;
+    if (j > 0) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+    }
+    if (j + 2 < kv_end) issue_tile(j + 2, S2{});
+    if (active(j + 1)) qk(S1{}, sn);
+    __builtin_amdgcn_sched_barrier(0);
+    if (active(j)) softmax_pv(j, masked(j), sc, stag);
+    sc[0] = sn[0];
+    sc[1] = sn[1];
+  };
+  int j = 0;
+  for (; j + kStages <= kv_end; j += kStages) {
+    tile(j, I0{});
+    tile(j + 1, I1{});
+    tile(j + 2, I2{});
+  }
+  if (j < kv_end) tile(j, I0{});
+  if (j + 1 < kv_end) tile(j + 1, I1{});
+
+  // O = acc * sV / l' and LSE = (m + log2 l' - log2 448) ln 2.
+  const float lt = halves_sum(l);
+  const float inv = lt == 0.f ? 0.f : sv_cur / lt;
+  if (qrow < N) {
+    __bf16* og = (__bf16*)a.o + base + (size_t)qrow * kD;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[mt][4 * g + 0] * inv, oacc[mt][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(oacc[mt][4 * g + 2] * inv, oacc[mt][4 * g + 3] * inv);
+        *(u32x2*)(og + mt * 32 + 8 * g + 4 * hh) = w;
+      }
+    if (hh == 0)
+      a.lse[(size_t)bh * N + qrow] = lt == 0.f ? -INFINITY : (m + fast_log2(lt) - kLog2_448) * kLn2;
+  }
+#endif
+}
+
+template <bool CAUSAL>
+hipError_t launch_attn(const Fp8FwdArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_fp8(int d, QuantArgs a, int B, int H, hipStream_t s) {
+  if (d == 64) return a.rot ? launch_quant_d<64, true>(a, B, H, s) : launch_quant_d<64, false>(a, B, H, s);
+  return a.rot ? launch_quant_d<128, true>(a, B, H, s) : launch_quant_d<128, false>(a, B, H, s);
+}
+
+hipError_t launch_fwd_fp8(int d, int causal, Fp8FwdArgs a, int B, int H, hipStream_t s) {
+  if (d != kD) return hipErrorNotSupported;
+  a.n_qtiles = (a.N + kBR - 1) / kBR;
+  const long long grid = (long long)B * H * a.n_qtiles;
+  a.remap = (grid % 8 == 0) ? 1 : 0;
+  return causal ? launch_attn<true>(a, (int)grid, s) : launch_attn<false>(a, (int)grid, s);
+}
+
 }  // namespace fa

@@ -24,8 +24,9 @@
  *     synchronises, and keeps no state apart from a thread-local error text.
  *   - Layout: contiguous row-major [B, H, N, d] for Q, K, V, O and the
  *     gradients; [B, H, N] float32 for LSE. B and H are batch dimensions.
- *   - d must be 64 or 128. B, H, N >= 1. scale must be finite and >= 0
- *     (the workloads use 1/sqrt(d)).
+ *   - d must be 64 or 128. B, H, N >= 1 with N * d <= 2^28 (one head is
+ *     addressed with 32-bit offsets) and B * H * N <= 2^31 - 1. scale must
+ *     be finite and >= 0 (the workloads use 1/sqrt(d)).
  *   - causal != 0 applies the lower-triangular mask: query i sees keys
  *     j <= i (the diagonal is kept). N queries and N keys.
  *   - LSE is the natural log of sum_j exp(scale * q_i . k_j) over the keys
@@ -122,19 +123,24 @@ FA_API int fa_bwd_f32(const float* q, const float* k, const float* v, const floa
  * block_rows = 0: one scale for the whole tensor (the per-tensor baseline).
  * scales: [B,H,ceil(N/64)] float32 (written; with block_rows = 0 every entry
  * holds the same value). s = amax / 448 in float32 (1 for an all-zero block);
- * x8 = e4m3fn(x / s), round to nearest even after saturating to +-448
- * (x8: [B,H,N,d] bytes, written). NaN inputs give the NaN code.
- * block_rows = 0 uses scales as scratch for a two-pass reduction. */
+ * x8 = e4m3fn(x / s) with x / s a correctly rounded float32 division,
+ * rounded to nearest even after saturating to +-448 (x8: [B,H,N,d] bytes,
+ * written). Inputs are expected finite: a NaN element gets the NaN code 0x7F
+ * and is left out of its block's amax.
+ * block_rows = 0 runs three launches and uses scales as scratch between
+ * them (every entry ends up holding the one scale). */
 FA_API int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, float* scales,
                  int B, int H, int N, int d, int block_rows, void* stream);
 
 /* Forward on fp8 inputs: q8, k8, v8 e4m3fn codes [B,H,N,d] with scales
  * sq, sk, sv [B,H,ceil(N/64)] as written by fa_quant_fp8 (the dequantised
- * value of a code is decode(code) * s of its 64-row block). Both products
- * run on fp8 MFMA with float32 accumulation; P~ = exp(S - m) is rounded to
- * e4m3 as e4m3(P~ * 448) for the product with V, while the row sum l uses
- * the float32 P~. o: [B,H,N,d] bf16 (written). lse: [B,H,N] float32. d must
- * be 128. */
+ * value of a code is decode(code) * s of its 64-row block). Keys are taken
+ * in tiles of 64 (one scale block each); m is the exact running maximum
+ * after each tile, P~ = exp(S - m) <= 1 is rounded to e4m3 as
+ * e4m3(P~ * 448) for the product with V, and the row sum l uses the float32
+ * P~. Both products run on fp8 matrix cores into float32 accumulators.
+ * o: [B,H,N,d] bf16 (written). lse: [B,H,N] float32 (written). d must be
+ * 128. */
 FA_API int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* v8,
                const float* sq, const float* sk, const float* sv,
                void* o, float* lse,

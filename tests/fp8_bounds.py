@@ -1,0 +1,93 @@
+"""Per-element error bound for the fp8 attention kernel against the oracle's fp8 emulation.
+
+The kernel and the emulation (oracle/fp8.py, fp8_attention_tiled) take the
+same steps on the same codes; they differ only in how the scores are formed:
+  * the fp8 matrix cores sum the 128 products of a score with a reduced
+    precision: measured on MI355X, the error of a 64-term fp8 product stays
+    below 1.7e-4 of the sum of the absolute products. The bound uses
+    EPS_MMA = 2^-11 (about 3x that);
+  * the float32 scaling, exp2 and max steps add a few float32 roundings.
+From a score error |dS_ij| <= delta_ij the bound follows the emulation's own
+steps:
+  * the running maximum after each tile moves by at most delta_i = max_j
+    delta_ij;
+  * P' = 448 exp(S - m) therefore moves by a factor of at most
+    exp(eta_i), eta_i = 2 delta_i;
+  * its e4m3 code can be any code between those of P' exp(-eta_i) and
+    P' exp(eta_i);
+  * the row sum l moves by the same factor, plus float32 summation;
+  * the P V product adds EPS_MMA of the sum of its absolute products;
+  * the bf16 output adds half a bf16 spacing.
+Everything here is float64 numpy. It uses the oracle's e4m3 codec and
+dequantisation, and only the codes, scales and parameters the emulation
+itself receives.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import fp8 as F
+
+EPS_MMA = 2.0 ** -11
+U32 = 2.0 ** -24
+
+
+def _bf16_half_ulp(x):
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 8)
+
+
+def bound_rows(q8, sq, k8, sk, v8, sv, scale, causal, rows, B_c=64):
+    """Bounds for |O_gpu - O_emul| ([len(rows), d]) and |LSE_gpu - LSE_emul| ([len(rows)]).
+
+    q8..sv are the codes and scales of one (batch, head): [N, d] and [ceil(N/64)].
+    Also returns the emulation's O for the rows, rebuilt from the same
+    quantities, as a cross-check of the bound's inputs.
+    """
+    N, d = q8.shape
+    rows = np.asarray(rows)
+    qd = F.dequantize(q8[None, None], sq[None, None])[0, 0][rows]
+    kd = F.dequantize(k8[None, None], sk[None, None])[0, 0]
+    vd = F.dequantize(v8[None, None], sv[None, None])[0, 0]
+    s = scale * (qd @ kd.T)
+    sabs = scale * (np.abs(qd) @ np.abs(kd).T)
+    keys = np.arange(N)
+    vis = np.ones_like(s, dtype=bool)
+    if causal:
+        vis = keys[None, :] <= rows[:, None]
+    s = np.where(vis, s, -np.inf)
+    # score error: matrix-core accumulation + float32 scaling / exp2 arguments
+    s_fin = np.where(vis, s, 0.0)
+    delta = np.where(vis, EPS_MMA * sabs + 8 * U32 * (np.abs(s_fin) + 1.0), 0.0)
+    dmax = delta.max(axis=1)
+    eta = 2.0 * dmax
+    # running maximum after each tile of B_c keys
+    t_c = -(-N // B_c)
+    tile_of = keys // B_c
+    tmax = np.stack([s[:, t * B_c:(t + 1) * B_c].max(axis=1) for t in range(t_c)], axis=1)
+    m_run = np.maximum.accumulate(tmax, axis=1)
+    m_fin = m_run[:, -1]
+    m_at = m_run[:, tile_of]                        # running max in force for key j
+    with np.errstate(invalid="ignore", over="ignore"):
+        p = np.where(vis, np.exp(s - m_at), 0.0)     # P~ of the emulation
+        w = np.where(vis, np.exp(m_at - m_fin[:, None]), 0.0)
+    l = (p * w).sum(axis=1)
+    pq = F.e4m3_decode(F.e4m3_encode(p.astype(np.float32) * np.float32(448.0)))
+    e = np.exp(eta)[:, None]
+    lo = F.e4m3_decode(F.e4m3_encode(np.minimum(p * 448.0 / e, 448.0)))
+    hi = F.e4m3_decode(F.e4m3_encode(np.minimum(p * 448.0 * e, 448.0)))
+    # weights of V_j in O: pq/448 * w / l; GPU: within the code range, with
+    # the rescale factors and l each off by at most exp(eta) (plus summation)
+    lsum = np.exp(eta + N * U32 * 4)[:, None]
+    a = pq / 448.0 * w / l[:, None]
+    a_hi = hi / 448.0 * w * e * lsum / l[:, None]
+    a_lo = lo / 448.0 * w / (e * lsum) / l[:, None]
+    da = np.maximum(a_hi - a, a - a_lo)
+    vabs = np.abs(vd)
+    o_emul = a @ vd
+    ob = da @ vabs + EPS_MMA * (a_hi @ vabs) * 2.0
+    ob += _bf16_half_ulp(np.abs(o_emul) + ob) + 1e-7
+    lse = m_fin + np.log(l)
+    lb = 3.0 * dmax + 4 * N * U32 + 4 * U32 * np.abs(lse) + 1e-6
+    return ob, lb, o_emul, lse

@@ -1,0 +1,262 @@
+"""fp8 path on the GPU ("FlashAttention v1～v4 完整进化史", v3 part 3).
+
+* Quantisation without rotation: codes and scales bit-exact against the
+  oracle's codec (the division x / s is float32 on both sides).
+* Quantisation with rotation: the GPU forms x * rot in float32; its codes must
+  lie within the codes of the exact product widened by the float32 summation
+  bound, and its scales within that bound of amax / 448.
+* fp8 attention: against the oracle's fp8 emulation on the same codes, element
+  by element, within the bound of tests/fp8_bounds.py (the matrix cores' fp8
+  accumulation, a few float32 roundings, e4m3 code flips they can cause, and
+  the bf16 output rounding).
+* Accuracy gate on the fp8 workload (B=4, H=32, N=8192, d=128, four outlier
+  channels x30, Haar rotation): per-64-row block scales + rotation must give an
+  RMSE of O (against the exact float64 attention of the bf16 inputs) at least
+  2x lower than one per-tensor scale without rotation.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from fp8_bounds import bound_rows
+from gpu_util import announce, dev_tensor
+from oracle import attention as A
+from oracle import fp8 as F
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    import exact_tiled_attention_12_amd as m
+    m.load()
+    return m
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _to_dev(a, dtype):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dtype).cuda()
+
+
+def _bf16_dev(vals):
+    import torch
+    bits, v = si.bf16_round(np.asarray(vals, dtype=np.float32))
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda(), v
+
+
+def _spread_inputs(w):
+    """Seeded bf16 values with tiny rows (subnormal codes), a zero block and large rows."""
+    x = si.make_inputs(w, names=("q",))["q"].copy()
+    B, H, N, d = x.shape
+    x[0, 0, : min(N, 5)] *= np.float32(1e-3)
+    if N > 128:
+        x[0, 1, 64:128] = 0.0
+    x[-1, -1, -1] *= np.float32(40.0)
+    return x
+
+
+@pytest.mark.parametrize("block_rows", [64, 0])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 200, 1000])
+def test_quant_exact(fa, block_rows, d, N):
+    w = si.Workload(960 + N, "quant", 2, 3, N, d, "bf16", False, False)
+    xt, xv = _bf16_dev(_spread_inputs(w))
+    codes_ref, s_ref, _ = F.quantize(xv, block_rows)
+    announce(f"fa_quant_fp8 block_rows={block_rows} d={d} N={N}")
+    x8, sc = fa.quant_fp8(xt, block_rows=block_rows)
+    _sync()
+    got_c, got_s = x8.cpu().numpy(), sc.cpu().numpy()
+    assert np.array_equal(got_s.view(np.uint32), s_ref.view(np.uint32)), "scales differ"
+    bad = np.argwhere(got_c != codes_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [17, 200, 1000])
+def test_quant_rotated(fa, d, N):
+    w = si.Workload(965 + N, "quant-rot", 2, 2, N, d, "bf16", False, False, outlier_frac=0.01,
+                    outlier_gain=30.0, rotate=True)
+    x = si.make_inputs(w, names=("q",))
+    xt, xv = _bf16_dev(x["q"])
+    rot = x["rot"]
+    import torch
+    announce(f"fa_quant_fp8 rotated d={d} N={N}")
+    x8, sc = fa.quant_fp8(xt, rot=_to_dev(rot, torch.float32), block_rows=64)
+    _sync()
+    got_c, got_s = x8.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
+    x64 = xv.astype(np.float64)
+    r64 = rot.astype(np.float64)
+    y = x64 @ r64
+    u = 2.0 ** -24
+    err = d * u / (1 - d * u) * (np.abs(x64) @ np.abs(r64))      # float32 FMA chain bound
+    nb = -(-N // 64)
+    for b in range(w.B):
+        for h in range(w.H):
+            for i in range(nb):
+                blk = slice(64 * i, 64 * i + 64)
+                amax = np.abs(y[b, h, blk]).max()
+                e = err[b, h, blk].max()
+                lo = (amax - e) / 448 * (1 - u)
+                hi = (amax + e) / 448 * (1 + u)
+                assert lo <= got_s[b, h, i] <= hi, (b, h, i, got_s[b, h, i], amax / 448)
+    srow = np.repeat(got_s, 64, axis=2)[:, :, :N, None]
+    qlo = (y - err) / srow * (1 - 2 * u)
+    qhi = (y + err) / srow * (1 + 2 * u)
+    lo_v = F.e4m3_decode(F.e4m3_encode(np.minimum(qlo, qhi)))
+    hi_v = F.e4m3_decode(F.e4m3_encode(np.maximum(qlo, qhi)))
+    got_v = F.e4m3_decode(got_c)
+    ok = (got_v >= lo_v) & (got_v <= hi_v)
+    assert ok.all(), f"{np.sum(~ok)} codes outside the float32-summation range"
+    ref_c, _, _ = F.quantize(xv, 64, rot)
+    print(f"rotated d={d} N={N}: {np.sum(got_c != ref_c)} of {got_c.size} codes differ from the float64 product's")
+
+
+def _fp8_codes(x, rot):
+    q8, sq, _ = F.quantize(x["q"], 64, rot)
+    k8, sk, _ = F.quantize(x["k"], 64, rot)
+    v8, sv, _ = F.quantize(x["v"], 64)
+    return q8, sq, k8, sk, v8, sv
+
+
+def _run_fwd_fp8(fa, codes, scale, causal):
+    import torch
+    q8, sq, k8, sk, v8, sv = codes
+    t = [_to_dev(a, torch.uint8) if a.dtype == np.uint8 else _to_dev(a, torch.float32) for a in codes]
+    o, lse = fa.fwd_fp8(t[0], t[2], t[4], t[1], t[3], t[5], causal=causal, scale=scale)
+    _sync()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _check_rows(o, lse, codes, b, h, rows, scale, causal):
+    q8, sq, k8, sk, v8, sv = codes
+    ob, lb, o_em, l_em = bound_rows(q8[b, h], sq[b, h], k8[b, h], sk[b, h], v8[b, h], sv[b, h], scale, causal, rows)
+    eo = np.abs(o[b, h][rows] - o_em)
+    el = np.abs(lse[b, h][rows] - l_em)
+    assert np.all(np.isfinite(o[b, h][rows])) and np.all(np.isfinite(lse[b, h][rows]))
+    ro, rl = float(np.max(eo / ob)), float(np.max(el / lb))
+    return ro, rl, float(eo.max()), float(el.max())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 200, 257, 1000])
+def test_fwd_fp8_against_emulation(fa, causal, N):
+    w = si.Workload(970 + N, "fp8 small", 1, 2, N, 128, "bf16", causal, False, outlier_frac=0.01,
+                    outlier_gain=30.0, rotate=True)
+    x = si.make_inputs(w, names=("q", "k", "v"))
+    codes = _fp8_codes(x, x["rot"])
+    announce(f"fa_fwd_fp8 N={N} causal={causal}")
+    o, lse = _run_fwd_fp8(fa, codes, w.scale, causal)
+    worst = (0.0, 0.0, 0.0, 0.0)
+    for h in range(w.H):
+        r = _check_rows(o, lse, codes, 0, h, np.arange(N), w.scale, causal)
+        worst = tuple(max(a, b) for a, b in zip(worst, r))
+    print(f"fp8 N={N} causal={causal}: O err/bound {worst[0]:.3f} (max {worst[2]:.2e}), "
+          f"LSE err/bound {worst[1]:.3f} (max {worst[3]:.2e})")
+    assert worst[0] <= 1.0 and worst[1] <= 1.0, worst
+
+
+@pytest.fixture(scope="module")
+def workload5(fa):
+    """GPU outputs of the fp8 workload, both quantisation schemes, plus the inputs."""
+    import torch
+    w = si.workload(5)
+    x = si.make_inputs(w, names=("q", "k", "v"))
+    dev = {n: dev_tensor(x, n, "bf16") for n in "qkv"}
+    rot = _to_dev(x["rot"], torch.float32)
+    out = {}
+    for name, br, use_rot in (("block", 64, True), ("tensor", 0, False)):
+        announce(f"workload 5: fa_quant_fp8 block_rows={br} rot={use_rot}")
+        q8, sq = fa.quant_fp8(dev["q"], rot=rot if use_rot else None, block_rows=br)
+        k8, sk = fa.quant_fp8(dev["k"], rot=rot if use_rot else None, block_rows=br)
+        v8, sv = fa.quant_fp8(dev["v"], block_rows=br)
+        announce(f"workload 5: fa_fwd_fp8 ({name})")
+        o, lse = fa.fwd_fp8(q8, k8, v8, sq, sk, sv, causal=False, scale=w.scale)
+        _sync()
+        out[name] = (o.float().cpu().numpy(), lse.cpu().numpy(), (q8, sq, k8, sk, v8, sv))
+    del dev
+    return w, x, out
+
+
+def _sample_heads(x, w):
+    heads = sorted({(0, int(h)) for h in x["outliers"][:, 0]})
+    rng = np.random.default_rng(5)
+    while len(heads) < 8:
+        bh = (int(rng.integers(w.B)), int(rng.integers(w.H)))
+        if bh not in heads:
+            heads.append(bh)
+    return heads
+
+
+def test_workload5_rmse_gate(workload5):
+    w, x, out = workload5
+    heads = _sample_heads(x, w)
+    se_blk = se_pt = 0.0
+    n = 0
+    for (b, h) in heads:
+        o_ex, _ = A.forward(x["q"][b, h], x["k"][b, h], x["v"][b, h], w.scale, False)
+        se_blk += float(np.sum((out["block"][0][b, h] - o_ex) ** 2))
+        se_pt += float(np.sum((out["tensor"][0][b, h] - o_ex) ** 2))
+        n += o_ex.size
+    r_blk, r_pt = np.sqrt(se_blk / n), np.sqrt(se_pt / n)
+    print(f"workload 5 RMSE over heads {heads}: block+rotation {r_blk:.4e}, per-tensor {r_pt:.4e}, "
+          f"ratio {r_pt / r_blk:.2f}")
+    assert r_pt / r_blk >= 2.0
+
+
+def test_workload5_per_tensor_matches_emulation_rmse(workload5):
+    """The GPU per-tensor baseline's RMSE agrees with the CPU emulation's within 10% (one outlier head)."""
+    w, x, out = workload5
+    b, h = 0, int(x["outliers"][0, 0])
+    o_ex, _ = A.forward(x["q"][b, h], x["k"][b, h], x["v"][b, h], w.scale, False)
+    codes = []
+    for n in "qkv":
+        # one scale for the whole tensor; the codes of the sampled head only
+        s = F.block_scales(x[n], 0)[b:b + 1, h:h + 1]
+        c = F.e4m3_encode((x[n][b:b + 1, h:h + 1].astype(np.float32) / s[0, 0, 0]).astype(np.float32))
+        codes += [c, s]
+    o_em, _ = F.fp8_attention_tiled(*codes, w.scale, False)
+    r_em = np.sqrt(np.mean((o_em[0, 0] - o_ex) ** 2))
+    r_gpu = np.sqrt(np.mean((out["tensor"][0][b, h] - o_ex) ** 2))
+    print(f"per-tensor RMSE head ({b},{h}): GPU {r_gpu:.4e}, emulation {r_em:.4e}")
+    assert abs(r_gpu - r_em) <= 0.1 * r_em
+
+
+def test_workload5_parity_sampled(fa, workload5):
+    """Full launch on codes from the oracle's quantiser for two sampled heads, rows checked by the bound."""
+    import torch
+    w, x, out = workload5
+    q8, sq, k8, sk, v8, sv = (t.clone() for t in out["block"][2])
+    heads = [(0, int(x["outliers"][0, 0])), (3, 11)]
+    host_codes = {}
+    for (b, h) in heads:
+        c = _fp8_codes({n: x[n][b:b + 1, h:h + 1] for n in "qkv"}, x["rot"])
+        host_codes[(b, h)] = c
+        for t, a in zip((q8, sq, k8, sk, v8, sv), c):
+            t[b, h] = torch.from_numpy(np.ascontiguousarray(a[0, 0])).to(t.dtype).cuda()
+    announce("workload 5: fa_fwd_fp8 on the oracle's codes")
+    o, lse = fa.fwd_fp8(q8, k8, v8, sq, sk, sv, causal=False, scale=w.scale)
+    _sync()
+    o, lse = o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(9)
+    worst = (0.0, 0.0, 0.0, 0.0)
+    for (b, h) in heads:
+        rows = np.sort(rng.choice(w.N, size=32, replace=False))
+        rows[-1] = w.N - 1
+        q8h, sqh, k8h, skh, v8h, svh = host_codes[(b, h)]
+        codes = tuple(a[0, 0][None, None] for a in (q8h, sqh, k8h, skh, v8h, svh))
+        r = _check_rows(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], codes, 0, 0, rows, w.scale, False)
+        worst = tuple(max(a, c) for a, c in zip(worst, r))
+    print(f"workload 5 sampled rows: O err/bound {worst[0]:.3f} (max {worst[2]:.2e}), "
+          f"LSE err/bound {worst[1]:.3f} (max {worst[3]:.2e})")
+    assert worst[0] <= 1.0 and worst[1] <= 1.0, worst
