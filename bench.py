@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_tiled_attention_12_amd", "csrc")
 
@@ -84,6 +85,57 @@ def cpu_baseline(heads: int):
                       f"float64 numpy, {dt:.1f} s"}
 
 
+def fp8_section(fa, steps: int, warmup: int):
+    """Times the fp8 workload (B=4, H=32, N=8192, d=128, non-causal): quantisation and attention.
+
+    Inputs: seeded N(0, 1) bf16 tensors drawn on the device, with the
+    workload's four shared outlier channels scaled by 30 in Q, K and V and a
+    seeded Haar rotation applied to Q and K by the quantiser.
+    """
+    import numpy as np
+    import torch
+    import seeded_inputs as si
+    w = si.workload(5)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    rng = np.random.default_rng(w.seed)
+    ch = si.outlier_channels(rng, H, d, w.outlier_frac)
+    rot = torch.from_numpy(si.haar_orthogonal(rng, d).astype(np.float32)).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)
+    x = {}
+    for n in "qkv":
+        t = torch.randn((B, H, N, d), device="cuda", generator=gen, dtype=torch.float32)
+        for hh, dd in ch:
+            t[:, int(hh), :, int(dd)] *= w.outlier_gain
+        x[n] = t.to(torch.bfloat16)
+        del t
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def run(e=None):
+        if e:
+            e[0].record()
+        q8, sq = fa.quant_fp8(x["q"], rot=rot)
+        k8, sk = fa.quant_fp8(x["k"], rot=rot)
+        v8, sv = fa.quant_fp8(x["v"])
+        if e:
+            e[1].record()
+        fa.fwd_fp8(q8, k8, v8, sq, sk, sv, causal=False, scale=w.scale)
+        if e:
+            e[2].record()
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        run(ev[i])
+    torch.cuda.synchronize()
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    f_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    tf = attention_flops(B, H, N, d, False) / (f_ms * 1e-3) / 1e12
+    return {"workload": "fp8 e4m3 attention, B=4 H=32 N=8192 d=128, non-causal, block scales + rotation",
+            "quant_ms": round(q_ms, 4), "fwd_ms": round(f_ms, 4), "fwd_tflops": round(tf, 2),
+            "fwd_frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +143,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 workload timing")
     ap.add_argument("--cpu-heads", type=int, default=1)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the warm-up, copy MIB MiB device-to-device once (a transfer of known "
@@ -205,6 +258,10 @@ def main():
                       "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if do_bwd else None},
         "roofline": roofline,
     }
+    if not args.no_fp8:
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+        out["fp8"] = fp8_section(fa, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_heads)
     print(json.dumps(out), flush=True)
