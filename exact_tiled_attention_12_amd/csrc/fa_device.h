@@ -53,6 +53,20 @@ __device__ __forceinline__ int acc_row_to_key(int i) {
 // Key held by accumulator slot r on lane half h (inverse view of the above).
 __host__ __device__ constexpr int slot_key(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
 
+// x *= s with the product written back into the register it was read from.
+// When an accumulator is rescaled on one branch only, a plain multiply lets
+// the register allocator give the product new registers and then copy the
+// untouched accumulator into them on the other branch; tying input and
+// output keeps one set of registers on both paths.
+__device__ __forceinline__ void scale_in_place(f32x16& x, float s) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float t = x[i];
+    asm("v_mul_f32 %0, %1, %0" : "+v"(t) : "v"(s));
+    x[i] = t;
+  }
+}
+
 // bf16 pair packing with round-to-nearest-even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   __bf16 a = (__bf16)lo, b = (__bf16)hi;

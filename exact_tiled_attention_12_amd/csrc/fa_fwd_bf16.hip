@@ -27,6 +27,7 @@
 //   * LDS rows are XOR-swizzled per 16-byte chunk so the K reads (16 rows, one
 //     chunk) and the transposed V reads (4 rows x 4 chunks) are free of bank
 //     conflicts.
+#include <cfloat>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -187,38 +188,41 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   };
 
   // Softmax of one 32-key block against the reference maximum, then
-  // O += V^T P^T over its 32 keys. MASK applies key < N and the causal
-  // condition (diagonal and ragged blocks only).
-  auto softmax_pv = [&](auto mask_tag, int u, f32x16& s, auto stag, int blk) __device__ {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    if constexpr (MASK) {
+  // O += V^T P^T over its 32 keys. `mask` applies key < N and the causal
+  // condition on ragged and diagonal blocks; a block above the diagonal of
+  // every row of the wave comes out fully masked and adds nothing. c > 0
+  // (the launcher clamps it), so masked scores stay -inf through the scaling.
+  auto softmax_pv = [&](bool mask, int u, f32x16& s, auto stag, int blk) __device__ {
+    if (mask) {
       const int key0 = u * 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + slot_key(r, hh);
         const bool ok = key < N && (!CAUSAL || key <= qrow);
-        s[r] = ok ? s[r] * c : -INFINITY;
+        s[r] = ok ? s[r] : -INFINITY;
       }
     }
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = halves_max(mx);
-    const float mxs = MASK ? mx : mx * c;
-    if (__builtin_amdgcn_ballot_w64(mxs > m_ref + kTau) != 0) {
-      const float m_new = fmaxf(m_ref, mxs);
-      const float alpha = fast_exp2(m_ref - m_new);
-      m_ref = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DBLK; ++db) oacc[db] *= alpha;
-    }
-    const float m_use = (MASK && m_ref == -INFINITY) ? 0.f : m_ref;
+    const float mxs = mx * c;
+    // Re-base only when the maximum grew by more than tau on some row of the
+    // wave (a wave-uniform decision). The accumulator is then scaled inside
+    // the first product of this block on one branch and fed unchanged on the
+    // other, so both branches end in a matrix-core write of the same
+    // registers and the untaken path costs no copies.
+    const bool grow = __builtin_amdgcn_ballot_w64(mxs > m_ref + kTau) != 0;
+    const float m_new = grow ? fmaxf(m_ref, mxs) : m_ref;
+    const float alpha = (!grow || m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
+    m_ref = m_new;
+    l *= alpha;
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     float part[4] = {0.f, 0.f, 0.f, 0.f};
     bf16x8 pf[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = MASK ? fast_exp2(s[r] - m_use) : fast_exp2(__builtin_fmaf(s[r], c, -m_use));
+      const float e = fast_exp2(__builtin_fmaf(s[r], c, -m_use));
       part[r & 3] += e;
       pf[r >> 3][r & 7] = (__bf16)e;
     }
@@ -226,45 +230,45 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     // V tile of `stage`, 16-key half ks of block blk: the key offset is a
     // compile-time immediate once blk and ks are.
     const unsigned char* vt = sp(stag) + C::TILE;
-    auto pv_half = [&](auto ofs_tag, int ks) __device__ {
+    auto read_v = [&](auto ofs_tag, bf16x8 (&vf)[C::DBLK]) __device__ {
       constexpr int OFS = decltype(ofs_tag)::value;
-      u32x2 v[2 * C::DBLK];
 #pragma unroll
       for (int db = 0; db < C::DBLK; ++db) {
         const unsigned char* vp = vt + (v_lane ^ (64u * db)) + OFS;
-        v[2 * db] = tr_read(vp);
-        v[2 * db + 1] = tr_read(vp + 4 * C::RB);
-      }
-#pragma unroll
-      for (int db = 0; db < C::DBLK; ++db) {
-        const u32x4 w = {v[2 * db][0], v[2 * db][1], v[2 * db + 1][0], v[2 * db + 1][1]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks], oacc[db], 0,
-                                                            0, 0);
+        const u32x2 v0 = tr_read(vp), v1 = tr_read(vp + 4 * C::RB);
+        const u32x4 w = {v0[0], v0[1], v1[0], v1[1]};
+        vf[db] = __builtin_bit_cast(bf16x8, w);
       }
     };
-    if (blk == 0) {
-      pv_half(std::integral_constant<int, 0>{}, 0);
-      pv_half(std::integral_constant<int, 16 * C::RB>{}, 1);
-    } else {
-      pv_half(std::integral_constant<int, 32 * C::RB>{}, 0);
-      pv_half(std::integral_constant<int, 48 * C::RB>{}, 1);
+    if (grow) {
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db) scale_in_place(oacc[db], alpha);
     }
+    auto pv = [&](auto ofs0, auto ofs1) __device__ {
+      bf16x8 vf[C::DBLK];
+      read_v(ofs0, vf);
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf[0], oacc[db], 0, 0, 0);
+      read_v(ofs1, vf);
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf[1], oacc[db], 0, 0, 0);
+    };
+    if (blk == 0)
+      pv(std::integral_constant<int, 0>{}, std::integral_constant<int, 16 * C::RB>{});
+    else
+      pv(std::integral_constant<int, 32 * C::RB>{}, std::integral_constant<int, 48 * C::RB>{});
   };
 
-  // 32-key blocks: u = 2*tile + blk. A wave computes block u only if some of
-  // its rows see a key of it; masking is needed on ragged and diagonal blocks.
-  const int n_blk = (N + 31) / 32;
-  const int u_end = CAUSAL ? min(n_blk, (min(q0 + kBR, N) - 1) / 32 + 1) : n_blk;
-  auto active = [&](int u) __device__ { return u < u_end && (!CAUSAL || u * 32 <= wrow0 + 31); };
+  // 32-key blocks: u = 2*tile + blk. Every wave runs every block of the
+  // workgroup's tiles (no divergent skips: they would make the accumulators
+  // change registers between branches); masking is needed on ragged and
+  // diagonal blocks, and blocks past a wave's last row are fully masked.
   auto masked = [&](int u) __device__ { return u * 32 + 32 > N || (CAUSAL && u * 32 + 31 > wrow0); };
   auto block = [&](int u, f32x16& cur, f32x16& nxt, auto stag, int blk, auto nstag, int nblk) __device__ {
-    if (active(u + 1)) qk(nstag, nblk, nxt);
-    if (active(u)) {
-      if (masked(u))
-        softmax_pv(std::true_type{}, u, cur, stag, blk);
-      else
-        softmax_pv(std::false_type{}, u, cur, stag, blk);
-    }
+    if (u + 1 < 2 * kv_end) qk(nstag, nblk, nxt);
+    softmax_pv(masked(u), u, cur, stag, blk);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -334,6 +338,10 @@ hipError_t launch(const FwdArgs& a, int grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(int d, int causal, FwdArgs a, int B, int H, hipStream_t s) {
+  // The kernel needs c > 0 so that -inf scores stay -inf after scaling; a
+  // zero scale becomes the smallest normal float, whose products with any
+  // finite score round exp2 to 1 exactly as scale 0 would.
+  a.c = fmaxf(a.c, FLT_MIN);
   a.n_qtiles = (a.N + kBR - 1) / kBR;
   const long long grid = (long long)B * H * a.n_qtiles;
   a.remap = (grid % 8 == 0) ? 1 : 0;
