@@ -10,20 +10,29 @@
 //   * one workgroup = 8 waves = 256 query rows of one (batch, head); each
 //     wave owns 32 rows; the grid issues the heaviest causal tiles first and
 //     groups the tiles of a (batch, head) on one XCD;
-//   * K and V tiles of 64 keys move from HBM straight into a 3-stage LDS ring
-//     (buffer loads with an LDS destination; rows past N read as zero), two
-//     tiles ahead of use, with one workgroup barrier per tile;
+//   * K and V tiles of 64 keys move from HBM straight into a 4-stage LDS ring
+//     (buffer loads with an LDS destination; rows past N read as zero),
+//     three tiles ahead of use, with one workgroup barrier per tile;
 //   * S^T = K Q^T and O^T = V^T P^T on the 32x32x16 bf16 MFMA: K rows are read
 //     in a permuted order so every lane owns one query and holds its
 //     exponentiated scores in exactly the operand layout of the second
 //     product; V stays row-major in LDS and is read transposed with
 //     ds_read_b64_tr_b16;
-//   * within a wave the loop is software-pipelined: the QK^T products of tile
-//     j+1 are issued while the softmax of tile j runs;
-//   * the running maximum is re-based only when it grows by more than
-//     tau = 8 (log2 units) on some row of the wave ("FlashAttention v1～v4
-//     完整进化史", v4 part 3); until then exponentials are taken against the
-//     stale maximum (they stay below 2^8), and O / l is exact at the end;
+//   * the work is a software pipeline over 32-key blocks: step u forms the
+//     exponentials of block u while the matrix cores run S of block u+1 and
+//     the product of block u-1 with V. None of the step's 16 products depends
+//     on its vector work, so the two are interleaved instruction by
+//     instruction (scheduling groups) and the matrix cores need not wait for
+//     the softmax;
+//   * lazy re-basing ("FlashAttention v1～v4 完整进化史", v4 part 3):
+//     exponentials are taken against a reference maximum m_ref that is moved
+//     only when needed. A step first exponentiates against the current
+//     m_ref; if the block sum of some lane is above 2^8 (or not finite, as in
+//     the first block, where m_ref = -inf), the wave takes the row maxima,
+//     re-bases every row to max(m_ref, row max), rescales l and the
+//     accumulator, and redoes the exponentials. Otherwise every exponential
+//     is below 2^8 and no maximum is formed at all. O / l and m_ref + log l
+//     are exact whatever m_ref is, so this only reorders the arithmetic;
 //   * LDS rows are XOR-swizzled per 16-byte chunk so the K reads (16 rows, one
 //     chunk) and the transposed V reads (4 rows x 4 chunks) are free of bank
 //     conflicts.
@@ -41,8 +50,13 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;   // query rows per workgroup
 constexpr int kBC = 64;            // keys per tile
-constexpr int kStages = 3;
-constexpr float kTau = 8.f;
+constexpr int kStages = 4;
+// A lane's exponent sum over one 16-score half block above this (2^8) or not
+// finite triggers a re-base; below it every exponential is below 2^8.
+constexpr float kPartMax = 256.f;
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -53,14 +67,19 @@ struct Cfg {
   static constexpr int CPR = RB / 16;               // 16-byte chunks per row
   static constexpr int TILE = kBC * RB;             // bytes of one K or V tile
   static constexpr int STAGE = 2 * TILE;
-  static constexpr int LDS_BYTES = kStages * STAGE;   // three __shared__ stages
+  static constexpr int LDS_BYTES = kStages * STAGE;
   static constexpr int LPW = TILE / 1024 / kWaves;  // 1 KiB wave-loads per wave per tensor
   static constexpr int RPL = 1024 / RB;             // rows per wave-load
+  static constexpr int LOADS = 2 * LPW;             // loads per wave per tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
   static_assert(LPW >= 1 && LPW * kWaves * 1024 == TILE, "tile split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(3 * LOADS <= 15, "vmcnt immediates below assume at most 15 loads in flight");
 };
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt(n) and lgkmcnt(0), expcnt left free.
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | (7 << 4); }
 
 // Physical chunk of logical chunk c in LDS row r. K: the 16 rows read together
 // by one 16-lane group land on 16 distinct bank groups. V: 4 consecutive rows
@@ -79,6 +98,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Workgroup barrier that orders LDS only: loads still in flight to other ring
+// stages stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // The body is compiled in the device pass only: the host pass needs just the
@@ -87,16 +114,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = Cfg<D>;
   // One variable per ring stage: with the stage known at compile time the
-  // compiler can tell a tile being read from the tile being loaded, and needs
+  // compiler can tell a tile being read from the tiles being loaded, and needs
   // no wait on the in-flight loads before the reads.
   __shared__ __attribute__((aligned(1024))) unsigned char st0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st3[C::STAGE];
   auto sp = [&](auto stag) -> unsigned char* {
     constexpr int S = decltype(stag)::value;
     if constexpr (S == 0) return st0;
     else if constexpr (S == 1) return st1;
-    else return st2;
+    else if constexpr (S == 2) return st2;
+    else return st3;
   };
 
   const int tid = threadIdx.x;
@@ -122,6 +151,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   const int n_kv = (N + kBC - 1) / kBC;
   const int kv_end = CAUSAL ? min(n_kv, (min(q0 + kBR, N) - 1) / kBC + 1) : n_kv;
+  const int U = 2 * kv_end;   // 32-key blocks
 
   // --- tile loads: HBM -> LDS, no registers. Wave-load t covers rows
   // [t*RPL, t*RPL+RPL) of the tile; lane l fills physical chunk l % CPR of
@@ -174,141 +204,183 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < C::DBLK; ++i) oacc[i] = f32x16{};
 
-  // S^T of one 32-key block (blk) of the tile in stage `stag`.
-  auto qk = [&](auto stag, int blk, f32x16& s) __device__ {
-    const unsigned char* kt = sp(stag);
-    f32x16 acc = f32x16{};
+  // K fragments of 32-key block `kblk` of the tile in stage `kst`.
+  auto read_k = [&](auto kst, auto kblk, bf16x8 (&kf)[C::KSTEPS]) __device__ {
+    const unsigned char* kt = sp(kst) + decltype(kblk)::value * 32 * C::RB;
 #pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      const unsigned addr = (k_lane ^ (32u * kk)) + blk * 32 * C::RB;
-      const bf16x8 af = *LDS(bf16x8, kt + addr);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], acc, 0, 0, 0);
-    }
-    s = acc;
+    for (int kk = 0; kk < C::KSTEPS; ++kk) kf[kk] = *LDS(bf16x8, kt + (k_lane ^ (32u * kk)));
   };
-
-  // Softmax of one 32-key block against the reference maximum, then
-  // O += V^T P^T over its 32 keys. `mask` applies key < N and the causal
-  // condition on ragged and diagonal blocks; a block above the diagonal of
-  // every row of the wave comes out fully masked and adds nothing. c > 0
-  // (the launcher clamps it), so masked scores stay -inf through the scaling.
-  auto softmax_pv = [&](bool mask, int u, f32x16& s, auto stag, int blk) __device__ {
-    if (mask) {
-      const int key0 = u * 32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + slot_key(r, hh);
-        const bool ok = key < N && (!CAUSAL || key <= qrow);
-        s[r] = ok ? s[r] : -INFINITY;
-      }
-    }
-    float mx = s[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = halves_max(mx);
-    const float mxs = mx * c;
-    // Re-base only when the maximum grew by more than tau on some row of the
-    // wave (a wave-uniform decision). The accumulator is then scaled inside
-    // the first product of this block on one branch and fed unchanged on the
-    // other, so both branches end in a matrix-core write of the same
-    // registers and the untaken path costs no copies.
-    const bool grow = __builtin_amdgcn_ballot_w64(mxs > m_ref + kTau) != 0;
-    const float m_new = grow ? fmaxf(m_ref, mxs) : m_ref;
-    const float alpha = (!grow || m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
-    m_ref = m_new;
-    l *= alpha;
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 pf[2];
+  // Scores of block u that are past N or (causal) above the diagonal -> -inf.
+  // Needed on ragged and diagonal blocks only; blocks entirely past the last
+  // row of the wave come out fully masked and add nothing.
+  auto masked = [&](int u) __device__ { return u * 32 + 32 > N || (CAUSAL && u * 32 + 31 > wrow0); };
+  auto apply_mask = [&](int u, f32x16& s) __device__ {
+    const int key0 = u * 32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(__builtin_fmaf(s[r], c, -m_use));
-      part[r & 3] += e;
-      pf[r >> 3][r & 7] = (__bf16)e;
+      const int key = key0 + slot_key(r, hh);
+      const bool ok = key < N && (!CAUSAL || key <= qrow);
+      s[r] = ok ? s[r] : -INFINITY;
     }
-    l += (part[0] + part[1]) + (part[2] + part[3]);
-    // V tile of `stage`, 16-key half ks of block blk: the key offset is a
-    // compile-time immediate once blk and ks are.
-    const unsigned char* vt = sp(stag) + C::TILE;
-    auto read_v = [&](auto ofs_tag, bf16x8 (&vf)[C::DBLK]) __device__ {
-      constexpr int OFS = decltype(ofs_tag)::value;
+  };
+
+  // Exponentials of one block against m_sub, packed to bf16 as the operand of
+  // the product with V; returns this lane's sum of the (unrounded) values.
+  // c > 0 (the launcher clamps it), so masked scores give exactly 0.
+  auto exps = [&](const f32x16& s, float m_sub, bf16x8 (&p)[2]) __device__ -> float {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int db = 0; db < C::DBLK; ++db) {
-        const unsigned char* vp = vt + (v_lane ^ (64u * db)) + OFS;
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(__builtin_fmaf(s[r], c, -m_sub));
+      part[r & 3] += e;
+      p[r >> 3][r & 7] = (__bf16)e;
+    }
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  };
+
+  // One pipeline step: softmax of block u (scores in s_cur, bf16 result to
+  // p_cur), S of block u+1 (K from stage kst) into s_nxt, and O += V^T P^T of
+  // block u-1 (p_prev, V from stage vst). The 2*KSTEPS products alternate
+  // between the two chains (even position: S, odd: O); each position also
+  // issues the LDS reads of the product AHEAD positions later and forms an
+  // equal share of the 16 exponentials. Scheduling fences between positions
+  // keep this order, so the matrix core always has the next product queued
+  // while the vector unit works on the exponentials.
+  auto step = [&](int u, f32x16& s_cur, f32x16& s_nxt, const bf16x8 (&p_prev)[2], bf16x8 (&p_cur)[2],
+                  auto kst, auto kblk, auto vst, auto vblk) __device__ {
+    if (masked(u)) apply_mask(u, s_cur);
+    constexpr int NM = 2 * C::KSTEPS;   // products per step
+    constexpr int SPM = 16 / NM;        // exponentials per product
+    constexpr int AHEAD = 3;
+    const unsigned char* kt = sp(kst) + decltype(kblk)::value * 32 * C::RB;
+    const unsigned char* vt = sp(vst) + C::TILE + decltype(vblk)::value * 32 * C::RB;
+    bf16x8 kf[C::KSTEPS];
+    bf16x8 vf[2 * C::DBLK];
+    auto fetch = [&](int i) __device__ {
+      if (i % 2 == 0) {
+        kf[i / 2] = *LDS(bf16x8, kt + (k_lane ^ (32u * (i / 2))));
+      } else {
+        const int h = (i / 2) / C::DBLK, db = (i / 2) % C::DBLK;
+        const unsigned char* vp = vt + (v_lane ^ (64u * db)) + h * 16 * C::RB;
         const u32x2 v0 = tr_read(vp), v1 = tr_read(vp + 4 * C::RB);
         const u32x4 w = {v0[0], v0[1], v1[0], v1[1]};
-        vf[db] = __builtin_bit_cast(bf16x8, w);
+        vf[i / 2] = __builtin_bit_cast(bf16x8, w);
       }
     };
-    if (grow) {
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) fetch(i);
+    f32x16 acc = f32x16{};
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float e_prev = 0.f;
+    const float neg_m = -m_ref;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + AHEAD < NM) fetch(i + AHEAD);
+      if (i % 2 == 0) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i / 2], qf[i / 2], acc, 0, 0, 0);
+      } else {
+        const int h = (i / 2) / C::DBLK, db = (i / 2) % C::DBLK;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i / 2], p_prev[h], oacc[db], 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < SPM; ++k) {
+        const int r = i * SPM + k;
+        const float e = fast_exp2(__builtin_fmaf(s_cur[r], c, neg_m));
+        part[r & 3] += e;
+        if (r & 1) {
+          p_cur[r >> 3][(r & 7) - 1] = (__bf16)e_prev;
+          p_cur[r >> 3][r & 7] = (__bf16)e;
+        }
+        e_prev = e;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s_nxt = acc;
+    float sum = (part[0] + part[1]) + (part[2] + part[3]);
+    if (__builtin_amdgcn_ballot_w64(!(sum <= kPartMax)) != 0) {
+      // Re-base every row of the wave to max(m_ref, row maximum of block u).
+      float mx = s_cur[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+      mx = halves_max(mx);
+      const float m_new = fmaxf(m_ref, mx * c);
+      const float alpha = m_new == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      l *= alpha;
 #pragma unroll
       for (int db = 0; db < C::DBLK; ++db) scale_in_place(oacc[db], alpha);
+      sum = exps(s_cur, m_ref == -INFINITY ? 0.f : m_ref, p_cur);
     }
-    auto pv = [&](auto ofs0, auto ofs1) __device__ {
-      bf16x8 vf[C::DBLK];
-      read_v(ofs0, vf);
-#pragma unroll
-      for (int db = 0; db < C::DBLK; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf[0], oacc[db], 0, 0, 0);
-      read_v(ofs1, vf);
-#pragma unroll
-      for (int db = 0; db < C::DBLK; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf[1], oacc[db], 0, 0, 0);
-    };
-    if (blk == 0)
-      pv(std::integral_constant<int, 0>{}, std::integral_constant<int, 16 * C::RB>{});
+    l += sum;
+  };
+
+  // Ring bookkeeping before step 2j+1: tile j+1 must be resident (its K is
+  // read by that step); tile j-1 was last read by step 2j, so its stage takes
+  // tile j+3.
+  auto tile_sync = [&](int j, auto nst) __device__ {
+    if (j + 2 < kv_end)
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(C::LOADS));
     else
-      pv(std::integral_constant<int, 32 * C::RB>{}, std::integral_constant<int, 48 * C::RB>{});
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    lds_barrier();
+    if (j + 3 < kv_end) issue_tile(j + 3, nst);
   };
 
-  // 32-key blocks: u = 2*tile + blk. Every wave runs every block of the
-  // workgroup's tiles (no divergent skips: they would make the accumulators
-  // change registers between branches); masking is needed on ragged and
-  // diagonal blocks, and blocks past a wave's last row are fully masked.
-  auto masked = [&](int u) __device__ { return u * 32 + 32 > N || (CAUSAL && u * 32 + 31 > wrow0); };
-  auto block = [&](int u, f32x16& cur, f32x16& nxt, auto stag, int blk, auto nstag, int nblk) __device__ {
-    if (u + 1 < 2 * kv_end) qk(nstag, nblk, nxt);
-    softmax_pv(masked(u), u, cur, stag, blk);
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
+  // Prologue: tiles 0..2 in flight, S of block 0, then step 0 (its product
+  // with V is of a zero P against tile 0's V, which is finite).
+  issue_tile(0, IC<0>{});
+  if (kv_end > 1) issue_tile(1, IC<1>{});
+  if (kv_end > 2) issue_tile(2, IC<2>{});
+  if (kv_end > 2)
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * C::LOADS));
+  else if (kv_end > 1)
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(C::LOADS));
+  else
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  lds_barrier();
 
-  // Prologue: tiles 0 and 1 in flight, S of block 0.
-  issue_tile(0, I0{});
-  if (kv_end > 1) issue_tile(1, I1{});
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
   f32x16 sa, sb;
-  qk(I0{}, 0, sa);
-
-  // Tile j (in stage j % 3): blocks 2j (S in sa) and 2j+1; the next block's
-  // QK^T is issued alongside each softmax. The barrier makes tile j+1
-  // resident and frees the stage of tile j-1 for tile j+2. The loop is
-  // unrolled by the ring depth so every stage is a compile-time variable.
-  auto tile = [&](int j, auto stag) __device__ {
-    constexpr int S = decltype(stag)::value;
-    using S1 = std::integral_constant<int, (S + 1) % kStages>;
-    using S2 = std::integral_constant<int, (S + 2) % kStages>;
-    if (j > 0) {
-      // The compiler does not order LDS-destination loads before a barrier by
-      // itself: wait for this wave's loads of tile j+1 (the only ones in
-      // flight), then the barrier publishes every wave's part.
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-    }
-    if (j + 2 < kv_end) issue_tile(j + 2, S2{});
-    block(2 * j, sa, sb, stag, 0, stag, 1);
-    block(2 * j + 1, sb, sa, stag, 1, S1{}, 0);
-  };
-  int j = 0;
-  for (; j + kStages <= kv_end; j += kStages) {
-    tile(j, I0{});
-    tile(j + 1, I1{});
-    tile(j + 2, I2{});
+  bf16x8 pa[2], pb[2] = {bf16x8{}, bf16x8{}};
+  {
+    bf16x8 kf[C::KSTEPS];
+    read_k(IC<0>{}, IC<0>{}, kf);
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], acc, 0, 0, 0);
+    sa = acc;
   }
-  if (j < kv_end) tile(j, I0{});
-  if (j + 1 < kv_end) tile(j + 1, I1{});
+  step(0, sa, sb, pb, pa, IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{});
+
+  // Steps 1..U, eight per iteration so that every ring stage is a
+  // compile-time variable. Step u reads K of block u+1 (tile (u+1)/2) and V of
+  // block u-1 (tile (u-1)/2). Step U is a drain: its block lies wholly past
+  // the last key (non-causal) or above the diagonal (causal), so the mask
+  // zeroes its exponentials, and it completes the product of block U-1; the K
+  // it reads is never used.
+  auto one = [&](auto s_tag, int u0) __device__ -> bool {
+    constexpr int S = decltype(s_tag)::value;
+    const int u = u0 + S;
+    using KST = IC<((S + 2) / 2) % kStages>;
+    using VST = IC<(S / 2) % kStages>;
+    using BLK = IC<S % 2>;
+    if constexpr (S % 2 == 0) {
+      tile_sync((u - 1) / 2, IC<(S / 2 + 3) % kStages>{});
+      step(u, sb, sa, pa, pb, KST{}, BLK{}, VST{}, BLK{});
+    } else {
+      step(u, sa, sb, pb, pa, KST{}, BLK{}, VST{}, BLK{});
+    }
+    return u == U;
+  };
+  for (int u0 = 1;; u0 += 8) {
+    if (one(IC<0>{}, u0)) break;
+    if (one(IC<1>{}, u0)) break;
+    if (one(IC<2>{}, u0)) break;
+    if (one(IC<3>{}, u0)) break;
+    if (one(IC<4>{}, u0)) break;
+    if (one(IC<5>{}, u0)) break;
+    if (one(IC<6>{}, u0)) break;
+    if (one(IC<7>{}, u0)) break;
+  }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) ln 2 in natural-log units.
   const float lt = halves_sum(l);
