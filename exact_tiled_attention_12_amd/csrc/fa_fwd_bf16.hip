@@ -10,9 +10,11 @@
 //   * one workgroup = 8 waves = 256 query rows of one (batch, head); each
 //     wave owns 32 rows; the grid issues the heaviest causal tiles first and
 //     groups the tiles of a (batch, head) on one XCD;
-//   * K and V tiles of 64 keys move from HBM straight into a 4-stage LDS ring
-//     (buffer loads with an LDS destination; rows past N read as zero),
-//     three tiles ahead of use, with one workgroup barrier per tile;
+//   * K and V tiles of 64 keys move from HBM straight into a 5-stage LDS ring
+//     (buffer loads with an LDS destination; rows past N read as zero), with
+//     one workgroup barrier per tile; a tile is resident two steps before
+//     its first read so that each step can fetch the first operands of the
+//     next one;
 //   * S^T = K Q^T and O^T = V^T P^T on the 32x32x16 bf16 MFMA: K rows are read
 //     in a permuted order so every lane owns one query and holds its
 //     exponentiated scores in exactly the operand layout of the second
@@ -50,7 +52,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;   // query rows per workgroup
 constexpr int kBC = 64;            // keys per tile
-constexpr int kStages = 4;
+constexpr int kStages = 5;
 // A lane's exponent sum over one 16-score half block above this (2^8) or not
 // finite triggers a re-base; below it every exponential is below 2^8.
 constexpr float kPartMax = 256.f;
@@ -60,6 +62,9 @@ using IC = std::integral_constant<int, N>;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+// The kernel body is built from lambdas; each must be inlined (a call would
+// move the accumulators through scratch memory).
+#define INL __attribute__((always_inline)) __device__
 
 template <int D>
 struct Cfg {
@@ -73,13 +78,13 @@ struct Cfg {
   static constexpr int LOADS = 2 * LPW;             // loads per wave per tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
-  static_assert(LPW >= 1 && LPW * kWaves * 1024 == TILE, "tile split");
+  static_assert((LPW == 1 || LPW == 2) && LPW * kWaves * 1024 == TILE, "tile split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(3 * LOADS <= 15, "vmcnt immediates below assume at most 15 loads in flight");
+  static_assert(2 * LOADS <= 15, "vmcnt immediates below assume waits for at most 15 loads");
 };
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt(n) and lgkmcnt(0), expcnt left free.
-constexpr int wait_vm_lgkm0(int n) { return (n & 15) | (7 << 4); }
+// s_waitcnt immediate (gfx9 encoding): vmcnt(n) only (n < 16).
+constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8); }
 
 // Physical chunk of logical chunk c in LDS row r. K: the 16 rows read together
 // by one 16-lane group land on 16 distinct bank groups. V: 4 consecutive rows
@@ -98,9 +103,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Workgroup barrier that orders LDS only: loads still in flight to other ring
-// stages stay in flight.
-__device__ __forceinline__ void lds_barrier() {
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The same raw buffer resource (base, num_records = bytes, no stride) as four
+// scalar words, for the LDS-destination loads below.
+__device__ __forceinline__ i32x4 dma_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(unsigned)b),
+               __builtin_amdgcn_readfirstlane((int)((unsigned)(b >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset `voffset` (past num_records: zeros) to
+// LDS byte address lds_addr + 16 * lane; lds_addr is wave-uniform and goes in
+// M0. Written as inline assembly so that the compiler does not count the copy
+// as a pending writer of the ring: it would otherwise wait for every copy in
+// flight before LDS reads of other stages. The kernel orders the copies
+// itself (vmcnt waits and barriers).
+__device__ __forceinline__ void dma_load16(i32x4 rsrc, unsigned lds_addr, unsigned voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voffset), "s"(rsrc) : "memory", "m0");
+}
+
+// Workgroup barrier for the LDS ring, ordering LDS only: each wave first
+// waits (vmcnt) for its own loads of the tile to land; loads still in flight
+// to other stages stay in flight.
+__device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -120,12 +148,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st2[C::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st3[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st4[C::STAGE];
   auto sp = [&](auto stag) -> unsigned char* {
     constexpr int S = decltype(stag)::value;
     if constexpr (S == 0) return st0;
     else if constexpr (S == 1) return st1;
     else if constexpr (S == 2) return st2;
-    else return st3;
+    else if constexpr (S == 3) return st3;
+    else return st4;
   };
 
   const int tid = threadIdx.x;
@@ -142,8 +172,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const size_t base = (size_t)bh * (size_t)N * D;
   const unsigned head_bytes = (unsigned)N * C::RB;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)a.q + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)a.k + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + base, head_bytes);
+  const i32x4 rk = dma_rsrc((const __bf16*)a.k + base, head_bytes);
+  const i32x4 rv = dma_rsrc((const __bf16*)a.v + base, head_bytes);
 
   const int q0 = qt * kBR;
   const int wrow0 = q0 + wave * 32;
@@ -156,17 +186,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // --- tile loads: HBM -> LDS, no registers. Wave-load t covers rows
   // [t*RPL, t*RPL+RPL) of the tile; lane l fills physical chunk l % CPR of
   // row t*RPL + l / CPR with the logical chunk that the swizzle maps there.
-  auto issue_tile = [&](int j, auto stag) __device__ {
+  // Each wave issues 2*LPW loads (K and V, part i) per tile. A tile index at
+  // or past kv_end gets an offset past the buffer end: the load moves no data
+  // and writes zeros to a stage nobody reads, which keeps the number of loads
+  // in flight the same for every tile.
+  auto issue_load = [&](int j, auto stag, int i, bool is_v) INL {
+    const int tl = wave * C::LPW + i;
+    const int row = tl * C::RPL + lane / C::CPR;
+    const int p = lane % C::CPR;
+    const unsigned grow = j < kv_end ? (unsigned)(j * kBC + row) * C::RB : 0x80000000u;
+    const unsigned d = (unsigned)(uintptr_t)LDS(unsigned char, sp(stag)) + tl * 1024 + (is_v ? C::TILE : 0);
+    if (is_v)
+      dma_load16(rv, d, grow + 16 * (p ^ v_swz<D>(row)));
+    else
+      dma_load16(rk, d, grow + 16 * (p ^ k_swz<D>(row)));
+  };
+  auto issue_tile = [&](int j, auto stag) INL {
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
-      const int tl = wave * C::LPW + i;
-      const int row = tl * C::RPL + lane / C::CPR;
-      const int p = lane % C::CPR;
-      const unsigned grow = (unsigned)(j * kBC + row) * C::RB;
-      unsigned char* kd = sp(stag) + tl * 1024;
-      unsigned char* vd = kd + C::TILE;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS(void, kd), 16, grow + 16 * (p ^ k_swz<D>(row)), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS(void, vd), 16, grow + 16 * (p ^ v_swz<D>(row)), 0, 0, 0);
+      issue_load(j, stag, i, false);
+      issue_load(j, stag, i, true);
     }
   };
 
@@ -205,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   for (int i = 0; i < C::DBLK; ++i) oacc[i] = f32x16{};
 
   // K fragments of 32-key block `kblk` of the tile in stage `kst`.
-  auto read_k = [&](auto kst, auto kblk, bf16x8 (&kf)[C::KSTEPS]) __device__ {
+  auto read_k = [&](auto kst, auto kblk, bf16x8 (&kf)[C::KSTEPS]) INL {
     const unsigned char* kt = sp(kst) + decltype(kblk)::value * 32 * C::RB;
 #pragma unroll
     for (int kk = 0; kk < C::KSTEPS; ++kk) kf[kk] = *LDS(bf16x8, kt + (k_lane ^ (32u * kk)));
@@ -213,8 +252,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // Scores of block u that are past N or (causal) above the diagonal -> -inf.
   // Needed on ragged and diagonal blocks only; blocks entirely past the last
   // row of the wave come out fully masked and add nothing.
-  auto masked = [&](int u) __device__ { return u * 32 + 32 > N || (CAUSAL && u * 32 + 31 > wrow0); };
-  auto apply_mask = [&](int u, f32x16& s) __device__ {
+  auto masked = [&](int u) INL { return u * 32 + 32 > N || (CAUSAL && u * 32 + 31 > wrow0); };
+  auto apply_mask = [&](int u, f32x16& s) INL {
     const int key0 = u * 32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -227,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // Exponentials of one block against m_sub, packed to bf16 as the operand of
   // the product with V; returns this lane's sum of the (unrounded) values.
   // c > 0 (the launcher clamps it), so masked scores give exactly 0.
-  auto exps = [&](const f32x16& s, float m_sub, bf16x8 (&p)[2]) __device__ -> float {
+  auto exps = [&](const f32x16& s, float m_sub, bf16x8 (&p)[2]) INL -> float {
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -238,55 +277,81 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     return (part[0] + part[1]) + (part[2] + part[3]);
   };
 
-  // One pipeline step: softmax of block u (scores in s_cur, bf16 result to
-  // p_cur), S of block u+1 (K from stage kst) into s_nxt, and O += V^T P^T of
-  // block u-1 (p_prev, V from stage vst). The 2*KSTEPS products alternate
-  // between the two chains (even position: S, odd: O); each position also
-  // issues the LDS reads of the product AHEAD positions later and forms an
-  // equal share of the 16 exponentials. Scheduling fences between positions
-  // keep this order, so the matrix core always has the next product queued
-  // while the vector unit works on the exponentials.
-  auto step = [&](int u, f32x16& s_cur, f32x16& s_nxt, const bf16x8 (&p_prev)[2], bf16x8 (&p_cur)[2],
-                  auto kst, auto kblk, auto vst, auto vblk) __device__ {
-    if (masked(u)) apply_mask(u, s_cur);
-    constexpr int NM = 2 * C::KSTEPS;   // products per step
-    constexpr int SPM = 16 / NM;        // exponentials per product
-    constexpr int AHEAD = 3;
-    const unsigned char* kt = sp(kst) + decltype(kblk)::value * 32 * C::RB;
-    const unsigned char* vt = sp(vst) + C::TILE + decltype(vblk)::value * 32 * C::RB;
+  // Order of the 2*KSTEPS products of a step: S (K fragment i) and O (V
+  // fragment i) alternate, except that the last two S products come before
+  // the last two O products, so S of the next block is complete two products
+  // before the next step reads it.
+  constexpr int NM = 2 * C::KSTEPS;
+  auto pos_is_s = [](int p) constexpr { return p < NM - 4 ? p % 2 == 0 : (p == NM - 4 || p == NM - 3); };
+  auto pos_idx = [](int p) constexpr {
+    return p < NM - 4 ? p / 2 : (p == NM - 4 ? NM / 2 - 2 : p == NM - 3 ? NM / 2 - 1 : p == NM - 2 ? NM / 2 - 2 : NM / 2 - 1);
+  };
+  constexpr int AHEAD = 3;   // operands are read this many products ahead
+  struct Ops {
     bf16x8 kf[C::KSTEPS];
     bf16x8 vf[2 * C::DBLK];
-    auto fetch = [&](int i) __device__ {
-      if (i % 2 == 0) {
-        kf[i / 2] = *LDS(bf16x8, kt + (k_lane ^ (32u * (i / 2))));
-      } else {
-        const int h = (i / 2) / C::DBLK, db = (i / 2) % C::DBLK;
-        const unsigned char* vp = vt + (v_lane ^ (64u * db)) + h * 16 * C::RB;
-        const u32x2 v0 = tr_read(vp), v1 = tr_read(vp + 4 * C::RB);
-        const u32x4 w = {v0[0], v0[1], v1[0], v1[1]};
-        vf[i / 2] = __builtin_bit_cast(bf16x8, w);
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i) fetch(i);
+  };
+  // Operand of the product at position p, from the K tile kt / V tile vt.
+  auto fetch = [&](int p, Ops& o, const unsigned char* kt, const unsigned char* vt) INL {
+    const int i = pos_idx(p);
+    if (pos_is_s(p)) {
+      o.kf[i] = *LDS(bf16x8, kt + (k_lane ^ (32u * i)));
+    } else {
+      const int h = i / C::DBLK, db = i % C::DBLK;
+      const unsigned char* vp = vt + (v_lane ^ (64u * db)) + h * 16 * C::RB;
+      const u32x2 v0 = tr_read(vp), v1 = tr_read(vp + 4 * C::RB);
+      const u32x4 w = {v0[0], v0[1], v1[0], v1[1]};
+      o.vf[i] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+  auto ktile = [&](auto kst, auto kblk) INL -> const unsigned char* {
+    return sp(kst) + decltype(kblk)::value * 32 * C::RB;
+  };
+  auto vtile = [&](auto vst, auto vblk) INL -> const unsigned char* {
+    return sp(vst) + C::TILE + decltype(vblk)::value * 32 * C::RB;
+  };
+
+  // One pipeline step: softmax of block u (scores in s_cur, bf16 result to
+  // p_cur), S of block u+1 (K tile kt) into s_nxt, and O += V^T P^T of block
+  // u-1 (p_prev, V tile vt). Each position issues the LDS reads of the product
+  // AHEAD positions later (for the last positions, the first products of the
+  // next step, from its tiles nkt / nvt into `nxt`) and forms an equal share
+  // of the 16 exponentials. Scheduling fences between positions keep this
+  // order, so the matrix core always has the next product queued while the
+  // vector unit works on the exponentials.
+  auto step = [&](int u, f32x16& s_cur, f32x16& s_nxt, const bf16x8 (&p_prev)[2], bf16x8 (&p_cur)[2], Ops& cur,
+                  Ops& nxt, const unsigned char* kt, const unsigned char* vt, const unsigned char* nkt,
+                  const unsigned char* nvt, int ld_tile, auto ld_stage, auto ld_part) INL {
+    constexpr int LP = decltype(ld_part)::value;   // part of tile ld_tile to load, or -1
+    if (masked(u)) apply_mask(u, s_cur);
+    constexpr int SPM = 16 / NM;   // exponentials per product
     f32x16 acc = f32x16{};
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float part[4];
     float e_prev = 0.f;
     const float neg_m = -m_ref;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      if (i + AHEAD < NM) fetch(i + AHEAD);
-      if (i % 2 == 0) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i / 2], qf[i / 2], acc, 0, 0, 0);
+      if (i + AHEAD < NM)
+        fetch(i + AHEAD, cur, kt, vt);
+      else
+        fetch(i + AHEAD - NM, nxt, nkt, nvt);
+      // This step's share of the ring loads, one load per few products.
+      if constexpr (LP >= 0) {
+        if (i == 2) issue_load(ld_tile, ld_stage, LP, false);
+        if (i == NM / 2 + 2) issue_load(ld_tile, ld_stage, LP, true);
+      }
+      const int k = pos_idx(i);
+      if (pos_is_s(i)) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.kf[k], qf[k], acc, 0, 0, 0);
       } else {
-        const int h = (i / 2) / C::DBLK, db = (i / 2) % C::DBLK;
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i / 2], p_prev[h], oacc[db], 0, 0, 0);
+        const int h = k / C::DBLK, db = k % C::DBLK;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.vf[k], p_prev[h], oacc[db], 0, 0, 0);
       }
 #pragma unroll
-      for (int k = 0; k < SPM; ++k) {
-        const int r = i * SPM + k;
+      for (int t = 0; t < SPM; ++t) {
+        const int r = i * SPM + t;
         const float e = fast_exp2(__builtin_fmaf(s_cur[r], c, neg_m));
-        part[r & 3] += e;
+        part[r & 3] = r < 4 ? e : part[r & 3] + e;
         if (r & 1) {
           p_cur[r >> 3][(r & 7) - 1] = (__bf16)e_prev;
           p_cur[r >> 3][r & 7] = (__bf16)e;
@@ -314,33 +379,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     l += sum;
   };
 
-  // Ring bookkeeping before step 2j+1: tile j+1 must be resident (its K is
-  // read by that step); tile j-1 was last read by step 2j, so its stage takes
-  // tile j+3.
-  auto tile_sync = [&](int j, auto nst) __device__ {
-    if (j + 2 < kv_end)
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(C::LOADS));
-    else
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-    lds_barrier();
-    if (j + 3 < kv_end) issue_tile(j + 3, nst);
+  // Ring bookkeeping before step 2j+1. Tile j+2 must be resident: its K is
+  // fetched at the end of step 2j+2. Tile j+3 (issued during steps 2j-1 and
+  // 2j) stays in flight. Tile j-1 was last read in step 2j, so after the
+  // barrier its stage takes tile j+4, loaded during steps 2j+1 and 2j+2.
+  auto tile_sync = [&]() INL {
+    __builtin_amdgcn_s_waitcnt(wait_vm(C::LOADS));
+    ring_barrier();
   };
 
-  // Prologue: tiles 0..2 in flight, S of block 0, then step 0 (its product
-  // with V is of a zero P against tile 0's V, which is finite).
+  // Prologue: tiles 0..3 in flight, tiles 0 and 1 resident, S of block 0,
+  // then step 0 (its product with V is of a zero P against tile 0's V,
+  // which is finite).
   issue_tile(0, IC<0>{});
-  if (kv_end > 1) issue_tile(1, IC<1>{});
-  if (kv_end > 2) issue_tile(2, IC<2>{});
-  if (kv_end > 2)
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * C::LOADS));
-  else if (kv_end > 1)
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(C::LOADS));
-  else
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-  lds_barrier();
+  issue_tile(1, IC<1>{});
+  issue_tile(2, IC<2>{});
+  issue_tile(3, IC<3>{});
+  __builtin_amdgcn_s_waitcnt(wait_vm(2 * C::LOADS));
+  ring_barrier();
 
   f32x16 sa, sb;
   bf16x8 pa[2], pb[2] = {bf16x8{}, bf16x8{}};
+  Ops oa, ob;
   {
     bf16x8 kf[C::KSTEPS];
     read_k(IC<0>{}, IC<0>{}, kf);
@@ -349,29 +409,36 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     for (int kk = 0; kk < C::KSTEPS; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], acc, 0, 0, 0);
     sa = acc;
   }
-  step(0, sa, sb, pb, pa, IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{});
+#pragma unroll
+  for (int p = 0; p < AHEAD; ++p) fetch(p, oa, ktile(IC<0>{}, IC<1>{}), vtile(IC<0>{}, IC<0>{}));
+  step(0, sa, sb, pb, pa, oa, ob, ktile(IC<0>{}, IC<1>{}), vtile(IC<0>{}, IC<0>{}), ktile(IC<1>{}, IC<0>{}),
+       vtile(IC<0>{}, IC<0>{}), 0, IC<0>{}, IC<-1>{});
 
-  // Steps 1..U, eight per iteration so that every ring stage is a
-  // compile-time variable. Step u reads K of block u+1 (tile (u+1)/2) and V of
-  // block u-1 (tile (u-1)/2). Step U is a drain: its block lies wholly past
-  // the last key (non-causal) or above the diagonal (causal), so the mask
-  // zeroes its exponentials, and it completes the product of block U-1; the K
-  // it reads is never used.
-  auto one = [&](auto s_tag, int u0) __device__ -> bool {
+  // Steps 1..U, ten per iteration so that every ring stage is a compile-time
+  // variable. Step u reads K of block u+1 (tile (u+1)/2) and V of block u-1
+  // (tile (u-1)/2). Step U is a drain: its block lies wholly past the last
+  // key (non-causal) or above the diagonal (causal), so the mask zeroes its
+  // exponentials, and it completes the product of block U-1; the K it reads
+  // (and the operands it fetches for a step U+1) are never used.
+  auto one = [&](auto s_tag, int u0) INL -> bool {
     constexpr int S = decltype(s_tag)::value;
     const int u = u0 + S;
-    using KST = IC<((S + 2) / 2) % kStages>;
-    using VST = IC<(S / 2) % kStages>;
-    using BLK = IC<S % 2>;
+    const unsigned char* kt = ktile(IC<((S + 2) / 2) % kStages>{}, IC<S % 2>{});
+    const unsigned char* vt = vtile(IC<(S / 2) % kStages>{}, IC<S % 2>{});
+    const unsigned char* nkt = ktile(IC<((S + 3) / 2) % kStages>{}, IC<(S + 1) % 2>{});
+    const unsigned char* nvt = vtile(IC<((S + 1) / 2) % kStages>{}, IC<(S + 1) % 2>{});
+    // Tile j+4 (j = (u-1)/2) goes to the stage freed at the last barrier.
+    using LST = IC<(S / 2 + 4) % kStages>;
+    const int lt = (u - 1) / 2 + 4;
     if constexpr (S % 2 == 0) {
-      tile_sync((u - 1) / 2, IC<(S / 2 + 3) % kStages>{});
-      step(u, sb, sa, pa, pb, KST{}, BLK{}, VST{}, BLK{});
+      tile_sync();
+      step(u, sb, sa, pa, pb, ob, oa, kt, vt, nkt, nvt, lt, LST{}, IC<0>{});
     } else {
-      step(u, sa, sb, pb, pa, KST{}, BLK{}, VST{}, BLK{});
+      step(u, sa, sb, pb, pa, oa, ob, kt, vt, nkt, nvt, lt, LST{}, IC<C::LPW == 2 ? 1 : -1>{});
     }
     return u == U;
   };
-  for (int u0 = 1;; u0 += 8) {
+  for (int u0 = 1;; u0 += 2 * kStages) {
     if (one(IC<0>{}, u0)) break;
     if (one(IC<1>{}, u0)) break;
     if (one(IC<2>{}, u0)) break;
@@ -380,7 +447,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     if (one(IC<5>{}, u0)) break;
     if (one(IC<6>{}, u0)) break;
     if (one(IC<7>{}, u0)) break;
+    if (one(IC<8>{}, u0)) break;
+    if (one(IC<9>{}, u0)) break;
   }
+
+  // Loads of tiles past the end (zeros, into unread stages) may still be in
+  // flight; let them land before the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) ln 2 in natural-log units.
   const float lt = halves_sum(l);
