@@ -9,21 +9,26 @@
 // dQ is summed over key tiles with float32 atomics into the workspace.
 //
 // Schedule:
-//   * one workgroup (4 waves) per (batch, head, 256-key tile); each wave owns
-//     64 keys (two 32-key blocks); the dK and dV accumulators of those keys
-//     (2 x 64 x d floats) stay in registers for the whole pass, and V of the
-//     wave's keys is held as MFMA operands;
+//   * one workgroup (4 waves, one per SIMD) per (batch, head, 256-key tile);
+//     each wave owns 64 keys (two 32-key blocks); the dK and dV accumulators
+//     of those keys (2 x 64 x d floats) stay in the accumulation registers for
+//     the whole pass, and V of the wave's keys is held as MFMA operands;
 //   * the workgroup's K tile sits in LDS for the whole pass; query tiles of 32
-//     rows (Q, dO, L, D) stream through a 2-stage LDS ring with HBM->LDS
-//     buffer loads, one barrier per tile;
+//     rows (Q, dO, L, D) stream through a 3-stage LDS ring, copied from HBM
+//     two tiles ahead of use, one barrier per tile;
 //   * S = Q K^T and dP = dO V^T are formed with lanes = keys (Q and dO rows
 //     read in a permuted order), so the exponentiated P and dS come out in the
 //     operand layout of dV = P^T dO and dK = dS^T Q; the other orientation of
 //     Q and dO is read straight from the row-major tiles with
 //     ds_read_b64_tr_b16;
-//   * dS is written to LDS once (transposed, 16-byte writes) and dQ of tile
-//     i-1 is formed while tile i is processed: each wave takes one 32-column
-//     slice of dQ over all 256 keys (lanes = d) and adds it atomically;
+//   * dS is written to LDS once (transposed, 16-byte writes); dQ of tile i-1
+//     is formed during tile i: each wave takes one 32-column slice of dQ over
+//     all 256 keys (lanes = d) and adds it with buffer atomics;
+//   * one wave per SIMD means the wave itself must keep the matrix core fed:
+//     the products of a tile run in one interleaved stream (S and dP of tile
+//     i with dQ of tile i-1, then dV and dK), operands are read two products
+//     ahead, and the softmax work (P and dS) runs beside the dQ and dV/dK
+//     products instead of between them;
 //   * rows of the LDS tiles are XOR-swizzled per 16-byte chunk so that both
 //     the 16-row reads and the 4-row transposed reads hit distinct banks.
 #include "fa_device.h"
@@ -38,6 +43,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kKW = 64;              // keys per wave
 constexpr int kBC = kKW * kWaves;    // keys per workgroup
 constexpr int kBR = 32;              // query rows per tile
+constexpr int kStages = 3;           // query-tile ring depth
 
 #define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -47,19 +53,20 @@ struct Cfg {
   static constexpr int CPR = RB / 16;                // 16-byte chunks per row
   static constexpr int K_BYTES = kBC * RB;           // the workgroup's K tile
   static constexpr int QT = kBR * RB;                // one Q or dO tile
-  static constexpr int STAGE = 2 * QT + 2 * kBR * 4; // Q, dO, L, D
+  static constexpr int LD = 1024;                    // L (or D) region: one wave-load
+  static constexpr int STAGE = 2 * QT + 2 * LD;      // Q, dO, L, D
   static constexpr int DS_BYTES = kBC * kBR * 2;     // dS^T tile [key][q]
-  static constexpr int OFF_K = 0;
-  static constexpr int OFF_DS = OFF_K + K_BYTES;
-  static constexpr int OFF_RING = OFF_DS + 2 * DS_BYTES;
-  static constexpr int LDS_BYTES = OFF_RING + 2 * STAGE;
   static constexpr int RPL = 1024 / RB;              // rows per 1 KiB wave-load
   static constexpr int K_LOADS = K_BYTES / 1024 / kWaves;
   static constexpr int QT_LOADS = QT / 1024 / kWaves;
+  static constexpr int R_LOADS = 2 * QT_LOADS + 1;   // copies per wave per query tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
+  static constexpr int NQ = D == 128 ? 16 : 8;       // dQ products per wave per tile
+  static constexpr int LDS_BYTES = K_BYTES + 2 * DS_BYTES + kStages * STAGE;
   static_assert(QT_LOADS >= 1 && K_LOADS >= 1, "tile split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(R_LOADS + 32 <= 63, "vmcnt range");
 };
 
 // Swizzle of 16-byte chunks in rows of Q, dO and K tiles: conflict-free both
@@ -70,6 +77,7 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x2 tr_read(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, p)));
 }
@@ -85,23 +93,52 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// The same raw buffer resource as four scalar words, for the LDS-destination
+// copies below.
+__device__ __forceinline__ i32x4 dma_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(unsigned)b),
+               __builtin_amdgcn_readfirstlane((int)((unsigned)(b >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset `voffset` (past num_records: zeros) to
+// LDS byte address lds_addr + 16 * lane; lds_addr is wave-uniform (M0).
+// Inline assembly, so that the compiler does not count the copy as a pending
+// writer of the ring (it would wait for every copy in flight before any LDS
+// read); the kernel orders the copies itself with vmcnt waits and barriers.
+__device__ __forceinline__ void dma_load16(i32x4 rsrc, unsigned lds_addr, unsigned voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voffset), "s"(rsrc) : "memory", "m0");
+}
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt(n) only (n < 64).
+constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Workgroup barrier ordering LDS only (copies to other ring stages stay in
+// flight; each wave first waits for its own copies of the tile).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+#define INL __attribute__((always_inline)) __device__
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // Device pass only (the host pass needs just the launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = Cfg<D>;
-  // The K tile, the dS^T buffers and the query-tile ring are separate
-  // variables: while the next query tile is in flight into the ring only the
-  // K tile and dS^T are read, so the compiler needs no wait on the load.
   __shared__ __attribute__((aligned(1024))) unsigned char kt_s[C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char ds_s[2 * C::DS_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char rg_s[2 * C::STAGE];
-  auto ring = [&](int st) -> unsigned char* { return rg_s + st * C::STAGE; };
-  auto dsb = [&](int st) -> unsigned char* { return ds_s + st * C::DS_BYTES; };
+  __shared__ __attribute__((aligned(1024))) unsigned char rg_s[kStages * C::STAGE];
+  auto ring = [&](int st) INL -> unsigned char* { return rg_s + st * C::STAGE; };
+  auto dsb = [&](int b) INL -> unsigned char* { return ds_s + b * C::DS_BYTES; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -117,51 +154,54 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   const int N = a.N;
   const size_t base = (size_t)bh * (size_t)N * D;
   const unsigned head_bytes = (unsigned)N * C::RB;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)a.q + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)a.k + base, head_bytes);
+  const i32x4 rq = dma_rsrc((const __bf16*)a.q + base, head_bytes);
+  const i32x4 rk = dma_rsrc((const __bf16*)a.k + base, head_bytes);
+  const i32x4 rg = dma_rsrc((const __bf16*)a.dout + base, head_bytes);
+  const i32x4 rl = dma_rsrc(a.lse + (size_t)bh * N, (unsigned)N * 4);
+  const i32x4 rd = dma_rsrc(a.dvec + (size_t)bh * N, (unsigned)N * 4);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const __bf16*)a.dout + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + (size_t)bh * N, (unsigned)N * 4);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dvec + (size_t)bh * N, (unsigned)N * 4);
-  float* __restrict__ dQg = a.dq_acc + base;
+  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(a.dq_acc + base, (unsigned)N * D * 4);
 
   const int k0 = kt * kBC;
   const int kw0 = k0 + wave * kKW;
+  const unsigned kt_a = (unsigned)(uintptr_t)LDS(unsigned char, kt_s);
+  const unsigned rg_a = (unsigned)(uintptr_t)LDS(unsigned char, rg_s);
 
-  // ---- HBM -> LDS loads (rows past N read as zero).
-  auto load_rows = [&](const __amdgpu_buffer_rsrc_t& r, unsigned char* dst, int row0, int t) {
+  // ---- HBM -> LDS copies (rows past N, and tiles past the end, read as zero).
+  auto copy_rows = [&](const i32x4& r, unsigned dst, int row0, int t, bool live) INL {
     const int row = t * C::RPL + lane / C::CPR;
     const int p = lane % C::CPR;
-    const unsigned g = (unsigned)(row0 + row) * C::RB + 16 * (p ^ swz<D>(row));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS(void, dst + t * 1024), 16, g, 0, 0, 0);
+    const unsigned g = live ? (unsigned)(row0 + row) * C::RB + 16 * (p ^ swz<D>(row)) : 0x80000000u;
+    dma_load16(r, dst + t * 1024, g);
   };
-  auto issue_qtile = [&](int qt, int st) {
-    unsigned char* so = ring(st);
-#pragma unroll
-    for (int i = 0; i < C::QT_LOADS; ++i) {
-      const int t = wave * C::QT_LOADS + i;
-      load_rows(rq, so, qt * kBR, t);
-      load_rows(rg, so + C::QT, qt * kBR, t);
-    }
-    if (wave == 0) {
-      // L and D of the tile's 32 rows: 8 lanes x 16 bytes each.
-      if (lane < 8)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, LDS(void, so + 2 * C::QT), 16,
-                                                 (unsigned)(qt * kBR) * 4 + 16 * lane, 0, 0, 0);
-      else if (lane < 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, LDS(void, so + 2 * C::QT), 16,
-                                                 (unsigned)(qt * kBR) * 4 + 16 * (lane - 8), 0, 0, 0);
-    }
-  };
-
   const int n_qt = (N + kBR - 1) / kBR;
   const int qt_begin = CAUSAL ? k0 / kBR : 0;
-
-  // K tile (whole workgroup) and the first query tile.
+  const int nt = n_qt - qt_begin;   // query tiles this workgroup visits (>= 1)
+  // Every wave issues R_LOADS copies per tile: its share of Q and dO, and one
+  // copy of L (even waves) or D (odd waves) of the tile's 32 rows; lanes 8..63
+  // of that copy read past the row range and write zeros behind it. Two
+  // waves copy the same L or D bytes to the same place.
+  auto issue_qtile = [&](int i) INL {
+    const int qt = qt_begin + i;
+    const bool live = i < nt;
+    const unsigned so = rg_a + (i % kStages) * C::STAGE;
 #pragma unroll
-  for (int i = 0; i < C::K_LOADS; ++i) load_rows(rk, kt_s, k0, wave * C::K_LOADS + i);
-  if (qt_begin < n_qt) issue_qtile(qt_begin, 0);
+    for (int u = 0; u < C::QT_LOADS; ++u) {
+      const int t = wave * C::QT_LOADS + u;
+      copy_rows(rq, so, qt * kBR, t, live);
+      copy_rows(rg, so + C::QT, qt * kBR, t, live);
+    }
+    const unsigned lo = (unsigned)(qt * kBR) * 4 + 16 * lane;
+    const unsigned off = live && lane < 8 ? lo : 0x80000000u;
+    if (wave & 1)
+      dma_load16(rd, so + 2 * C::QT + C::LD, off);
+    else
+      dma_load16(rl, so + 2 * C::QT, off);
+  };
 
+  // K tile (whole workgroup), V operands, then the first two query tiles.
+#pragma unroll
+  for (int u = 0; u < C::K_LOADS; ++u) copy_rows(rk, kt_a, k0, wave * C::K_LOADS + u, true);
   // V rows of the wave's keys as the B operand of dP = dO V^T (lanes = keys).
   bf16x8 vf[2][C::KSTEPS];
 #pragma unroll
@@ -171,12 +211,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       const unsigned off = (unsigned)(kw0 + kb * 32 + l32) * C::RB + kk * 32 + hh * 16;
       vf[kb][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
+  issue_qtile(0);
+  issue_qtile(1);
 
   // ---- per-lane LDS addresses (byte offsets; chunk bits XORed per step).
   // Rows of a 32-row block read with lanes = one row each (Q, dO: permuted).
   const int prow = acc_row_to_key(l32);
-  const int fq = swz<D>(prow);
-  const unsigned a_lane = (unsigned)prow * C::RB + 16 * ((hh ^ fq) & 1) + 32 * (fq >> 1);
+  const int fq_ = swz<D>(prow);
+  const unsigned a_lane = (unsigned)prow * C::RB + 16 * ((hh ^ fq_) & 1) + 32 * (fq_ >> 1);
   const int fk = swz<D>(l32);
   const unsigned k_lane = (unsigned)(wave * kKW + l32) * C::RB + 16 * ((hh ^ fk) & 1) + 32 * (fk >> 1);
   // Transposed reads: source lane j = 4s + q of 16-lane group g points at row
@@ -197,6 +239,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
                    8 * (tq & 1);
   const unsigned w_lane = (unsigned)(wave * kKW + l32) * 64;   // dS^T write row base
   const int wsw = (l32 >> 2) & 3;
+  // dQ slice of this wave: column block db_q over keys [kc_q0, kc_q0 + NQ) x 16.
+  const int db_q = D == 128 ? wave : (wave & 1);
+  const int kc_q0 = D == 128 ? 0 : (wave >> 1) * 8;
 
   f32x16 dk[2][C::DBLK], dv[2][C::DBLK];
 #pragma unroll
@@ -208,103 +253,115 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     }
   const float c = a.c;
 
-  // dQ of the tile whose dS^T sits in dS buffer `st`: this wave's 32
-  // columns (D = 64: two waves per column block, each over half of the keys).
-  // Operand reads run one 16-key step ahead of the MFMAs.
-  auto dq_tile = [&](int qt, int st) {
+  // dQ operands (dS^T and K^T, transposed reads) of product m of the slice.
+  auto rd_dq = [&](const unsigned char* sb, int m) INL {
+    const int kc = kc_q0 + m;
+    Tr4 t;
+    t.v[0] = tr_read(sb + s_lane[0] + kc * 16 * 64);
+    t.v[1] = tr_read(sb + s_lane[1] + kc * 16 * 64);
+    t.v[2] = tr_read(kt_s + (t_lane[0] ^ (64u * db_q)) + kc * 16 * C::RB);
+    t.v[3] = tr_read(kt_s + (t_lane[1] ^ (64u * db_q)) + kc * 16 * C::RB);
+    return t;
+  };
+  // dQ atomics of the slice (rows of tile qt). A tile that does not exist (or
+  // rows past N) gets offsets past the buffer: the atomics are no-ops, so the
+  // number of memory operations per tile is the same everywhere.
+  auto dq_atomics = [&](const f32x16& acc, int qt, bool live) INL {
     const int q0 = qt * kBR;
-    int kc_end = kBC / 16;
-    if (CAUSAL) kc_end = min(kc_end, (q0 + kBR - 1 - k0) / 16 + 1);
-    const int db = D == 128 ? wave : (wave & 1);
-    const int kc0 = D == 128 ? 0 : (wave >> 1) * 8;
-    const int kc1 = D == 128 ? kc_end : min(kc_end, kc0 + 8);
-    const unsigned char* sb = dsb(st);
-    const unsigned char* s0a = sb + s_lane[0];
-    const unsigned char* s1a = sb + s_lane[1];
-    const unsigned char* k0a = kt_s + (t_lane[0] ^ (64u * db));
-    const unsigned char* k1a = kt_s + (t_lane[1] ^ (64u * db));
-    auto rd = [&](int kc) {
-      Tr4 t;
-      t.v[0] = tr_read(s0a + kc * 16 * 64);
-      t.v[1] = tr_read(s1a + kc * 16 * 64);
-      t.v[2] = tr_read(k0a + kc * 16 * C::RB);
-      t.v[3] = tr_read(k1a + kc * 16 * C::RB);
-      return t;
-    };
-    f32x16 acc = f32x16{};
-    if (kc0 < kc1) {
-      Tr4 cur = rd(kc0);
-      for (int kc = kc0; kc < kc1; ++kc) {
-        Tr4 nxt = cur;
-        if (kc + 1 < kc1) nxt = rd(kc + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        acc = mma(join(cur.v[0], cur.v[1]), join(cur.v[2], cur.v[3]), acc);
-        cur = nxt;
-      }
-      const int d = db * 32 + l32;
+    const int d = db_q * 32 + l32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (q < N) unsafeAtomicAdd(dQg + (size_t)q * D + d, acc[r]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const unsigned off = live && q < N ? ((unsigned)q * D + d) * 4 : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rdq, off, 0, 0);
     }
   };
 
-  // One query tile of this wave's 64 keys: S, dP, P, dS, dV, dK; dS^T to LDS.
-  // Q, dO, L, D come from ring stage `st`, dS^T goes to dS buffer `st`.
-  auto key_tile = [&](int qt, int st, bool mask, bool act) {
-    const int q0 = qt * kBR;
-    const unsigned char* qs = ring(st);
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    // Operand reads run one d-step ahead of the MFMAs (double buffer); the
-    // scheduling fences keep the compiler from hoisting every read at once.
-    bf16x8 fq[2], fg[2], fk0[2], fk1[2];
-    auto rd = [&](int kk, int b) {
-      fq[b] = *LDS(bf16x8, qs + (a_lane ^ (32u * kk)));
-      fg[b] = *LDS(bf16x8, qs + C::QT + (a_lane ^ (32u * kk)));
-      fk0[b] = *LDS(bf16x8, kt_s + (k_lane ^ (32u * kk)));
-      fk1[b] = *LDS(bf16x8, kt_s + (k_lane ^ (32u * kk)) + 32 * C::RB);
-    };
-    rd(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      const int b = kk & 1;
-      if (kk + 1 < C::KSTEPS) rd(kk + 1, b ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
-      s[0] = mma(fq[b], fk0[b], s[0]);
-      dp[0] = mma(fg[b], vf[0][kk], dp[0]);
-      s[1] = mma(fq[b], fk1[b], s[1]);
-      dp[1] = mma(fg[b], vf[1][kk], dp[1]);
-      __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS));   // K tile, V operands, query tile 0
+  lds_barrier();
+
+  // Query tile i (qt = qt_begin + i) is in ring stage i % 3; its dS^T goes to
+  // dS buffer i % 2, which dQ of tile i reads during tile i + 1.
+  for (int i = 0; i < nt; ++i) {
+    const int qt = qt_begin + i;
+    if (i > 0) {
+      // Copies issued after tile i's own: (i >= 2) the 16 atomics of tile
+      // i-2's dQ, then tile i+1 and the 16 atomics of tile i-1's dQ.
+      if (i == 1)
+        __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + 16));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + 32));
+      lds_barrier();
     }
-    // P = exp2(S c - L log2 e), dS = P (dP - D) at the 16 rows this lane
-    // holds. Entry (q0 + ql, key) is kept iff ql >= lim; on tiles that need
-    // no mask lim is below every ql, so one code path serves both.
-    const float* Ls = (const float*)(qs + 2 * C::QT);
-    const float* Ds = Ls + kBR;
-    bf16x8 pf[2][2], df[2][2];
+    issue_qtile(i + 2);   // into the stage of tile i-1, free after the barrier
+
+    const int q0 = qt * kBR;
+    const unsigned char* qs = ring(i % kStages);
+    const unsigned char* sb_prev = dsb((i + 1) & 1);
+    // Waves whose keys all follow the tile's rows run the tile fully masked.
+    const bool active = !CAUSAL || kw0 <= q0 + kBR - 1;
+    const bool mask = !active || kw0 + kKW > N || (CAUSAL && kw0 + kKW - 1 > q0);
     int lim[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = kw0 + kb * 32 + l32;
-      lim[kb] = !mask ? -1 : (!act || key >= N) ? kBR : CAUSAL ? key - q0 : -1;
+      lim[kb] = !mask ? -1 : (!active || key >= N) ? kBR : CAUSAL ? key - q0 : -1;
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
+
+    // L and D of the tile's rows (each lane reads those of its row slots).
+    const float* Ls = (const float*)(qs + 2 * C::QT);
+    const float* Ds = (const float*)(qs + 2 * C::QT + C::LD);
+    // Softmax of row slot r of key block kb: P = exp2(S c - L log2 e), dS =
+    // P (dP - D). Entry (q0 + ql, key) is kept iff ql >= lim.
+    f32x16 s[2], dp[2];
+    bf16x8 pf[2][2], df[2][2];
+    auto soft = [&](int kb, int r) INL {
       const int ql = slot_key(r, hh);
-      const float l2 = Ls[ql] * kLog2e, dd = Ds[ql];
+      const float l2 = *LDS(const float, Ls + ql) * kLog2e, dd = *LDS(const float, Ds + ql);
+      float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -l2));
+      p = ql >= lim[kb] ? p : 0.f;
+      const float ds = p * (dp[kb][r] - dd);
+      pf[kb][r >> 3][r & 7] = (__bf16)p;
+      df[kb][r >> 3][r & 7] = (__bf16)ds;
+    };
+
+    // ---- Phase 1: S and dP of tile i for key block 0, then for key block 1
+    // beside the softmax of block 0 (two evaluations per d step); operands
+    // read one step ahead.
+    bf16x8 fq[2], fg[2], fk[2];
+    auto rd_sdp = [&](int kb, int kk) INL {
+      const int b = kk % 2;
+      fq[b] = *LDS(bf16x8, qs + (a_lane ^ (32u * kk)));
+      fg[b] = *LDS(bf16x8, qs + C::QT + (a_lane ^ (32u * kk)));
+      fk[b] = *LDS(bf16x8, kt_s + (k_lane ^ (32u * kk)) + kb * 32 * C::RB);
+    };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -l2));
-        p = ql >= lim[kb] ? p : 0.f;
-        const float ds = p * (dp[kb][r] - dd);
-        pf[kb][r >> 3][r & 7] = (__bf16)p;
-        df[kb][r >> 3][r & 7] = (__bf16)ds;
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+      rd_sdp(kb, 0);
+      constexpr int SPK = 16 / C::KSTEPS;
+#pragma unroll
+      for (int kk = 0; kk < C::KSTEPS; ++kk) {
+        const int b = kk % 2;
+        if (kk + 1 < C::KSTEPS) rd_sdp(kb, kk + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        s[kb] = mma(fq[b], fk[b], s[kb]);
+        dp[kb] = mma(fg[b], vf[kb][kk], dp[kb]);
+        if (kb == 1) {
+#pragma unroll
+          for (int t = 0; t < SPK; ++t) soft(0, kk * SPK + t);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // dV += P^T dO, dK += dS^T Q: B operands read transposed from the tiles,
-    // one (ks, db) step ahead of the MFMAs.
-    auto trd = [&](int step) {
+
+    // ---- Phase 2: dV += P^T dO and dK += dS^T Q of key block 0 beside the
+    // softmax of key block 1; phase 3: the same products of key block 1 with
+    // dQ of tile i-1 (its dS^T is complete in LDS) interleaved. The B operands
+    // of dV and dK are read transposed from the ring one (ks, db) step ahead
+    // (once per key block); the dQ operands one product ahead.
+    auto trd = [&](int step) INL {
       const int ks = step / C::DBLK, db = step % C::DBLK;
       const unsigned char* ko = qs + ks * 16 * C::RB;
       Tr4 t;
@@ -314,58 +371,71 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       t.v[3] = tr_read(ko + (t_lane[1] ^ (64u * db)));
       return t;
     };
-    __builtin_amdgcn_sched_barrier(0);
-    Tr4 cur = trd(0);
-#pragma unroll
-    for (int step = 0; step < 2 * C::DBLK; ++step) {
+    constexpr int NS = 2 * C::DBLK;   // (ks, db) steps per key block
+    auto dvdk = [&](int kb, const Tr4& t, int step) INL {
       const int ks = step / C::DBLK, db = step % C::DBLK;
-      Tr4 nxt = cur;
-      if (step + 1 < 2 * C::DBLK) nxt = trd(step + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 gb = join(cur.v[0], cur.v[1]), qb = join(cur.v[2], cur.v[3]);
+      dv[kb][db] = mma(pf[kb][ks], join(t.v[0], t.v[1]), dv[kb][db]);
+      dk[kb][db] = mma(df[kb][ks], join(t.v[2], t.v[3]), dk[kb][db]);
+    };
+    Tr4 top[2];
+    top[0] = trd(0);
+    constexpr int SPS = 16 / NS;      // softmax evaluations per step
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        dv[kb][db] = mma(pf[kb][ks], gb, dv[kb][db]);
-        dk[kb][db] = mma(df[kb][ks], qb, dk[kb][db]);
+    for (int step = 0; step < NS; ++step) {
+      const int b = step % 2;
+      if (step + 1 < NS) top[(step + 1) % 2] = trd(step + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk(0, top[b], step);
+#pragma unroll
+      for (int t = 0; t < SPS; ++t) soft(1, step * SPS + t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+      // dS^T rows (keys) of this wave: 8 queries per 16-byte write.
+      unsigned char* sp = dsb(i & 1) + w_lane;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) *LDS(bf16x8, sp + kb * 32 * 64 + 16 * ((2 * k2 + hh) ^ wsw)) = df[kb][k2];
+    }
+    top[0] = trd(0);
+    Tr4 qop[2];
+    qop[0] = rd_dq(sb_prev, 0);
+    f32x16 dq_acc = f32x16{};
+    constexpr int QPS = C::NQ / NS;   // dQ products per step
+#pragma unroll
+    for (int step = 0; step < NS; ++step) {
+      const int b = step % 2;
+      if (step + 1 < NS) top[(step + 1) % 2] = trd(step + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk(1, top[b], step);
+#pragma unroll
+      for (int t = 0; t < QPS; ++t) {
+        const int m = step * QPS + t;
+        if (m + 1 < C::NQ) qop[(m + 1) % 2] = rd_dq(sb_prev, m + 1);
+        dq_acc = mma(join(qop[m % 2].v[0], qop[m % 2].v[1]), join(qop[m % 2].v[2], qop[m % 2].v[3]), dq_acc);
       }
-      cur = nxt;
       __builtin_amdgcn_sched_barrier(0);
     }
-    // dS^T rows (keys) of this wave: 8 queries per 16-byte write.
-    unsigned char* sp = dsb(st) + w_lane;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        *LDS(bf16x8, sp + kb * 32 * 64 + 16 * ((2 * ks + hh) ^ wsw)) = df[kb][ks];
-  };
-
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K tile, first query tile, V operands
-  __syncthreads();
-
-  // Query tile qt (i = qt - qt_begin) uses ring stage and dS buffer i % 2.
-  // After the barrier tile qt is resident and dS^T of tile qt-1 complete; the
-  // tile's own work reads the ring, then the load of tile qt+1 is queued into
-  // the other stage (free: its last reader was tile qt-1) and overlaps the dQ
-  // of tile qt-1, which reads only the K tile and dS^T.
-  for (int qt = qt_begin; qt < n_qt; ++qt) {
-    const int i = qt - qt_begin, st = i & 1;
-    if (i > 0) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's load of tile qt and its dQ atomics
-      __syncthreads();
-    }
-    // Waves whose keys all follow the tile's rows run the tile fully masked
-    // (one straight-line path keeps the accumulators in registers).
-    const int q0 = qt * kBR;
-    const bool active = !CAUSAL || kw0 <= q0 + kBR - 1;
-    const bool mask = !active || kw0 + kKW > N || (CAUSAL && kw0 + kKW - 1 > q0);
-    key_tile(qt, st, mask, active);
-    if (qt + 1 < n_qt) issue_qtile(qt + 1, st ^ 1);
-    if (i > 0) dq_tile(qt - 1, st ^ 1);
+    dq_atomics(dq_acc, qt - 1, i > 0);
   }
-  if (qt_begin < n_qt) {
-    __syncthreads();
-    dq_tile(n_qt - 1, (n_qt - 1 - qt_begin) & 1);
+
+  // dQ of the last tile.
+  lds_barrier();
+  {
+    const unsigned char* sb = dsb((nt - 1) & 1);
+    Tr4 qop[3];
+    qop[0] = rd_dq(sb, 0);
+    qop[1] = rd_dq(sb, 1);
+    f32x16 dq_acc = f32x16{};
+#pragma unroll
+    for (int m = 0; m < C::NQ; ++m) {
+      if (m + 2 < C::NQ) qop[(m + 2) % 3] = rd_dq(sb, m + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      dq_acc = mma(join(qop[m % 3].v[0], qop[m % 3].v[1]), join(qop[m % 3].v[2], qop[m % 3].v[3]), dq_acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    dq_atomics(dq_acc, qt_begin + nt - 1, true);
   }
 
   // Epilogue: dK = scale * acc, dV = acc (lanes = d, rows = keys); rows past N dropped.
@@ -385,6 +455,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, kv), rdk, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, vv), rdv, off, 0, 0);
       }
+  // Copies of tiles past the end (zeros into free ring stages) may still be
+  // in flight: let them land before the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
 #endif
 }
 
