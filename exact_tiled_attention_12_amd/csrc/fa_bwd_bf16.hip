@@ -21,14 +21,17 @@
 //     operand layout of dV = P^T dO and dK = dS^T Q; the other orientation of
 //     Q and dO is read straight from the row-major tiles with
 //     ds_read_b64_tr_b16;
-//   * dS is written to LDS once (transposed, 16-byte writes); dQ of tile i-1
-//     is formed during tile i: each wave takes one 32-column slice of dQ over
-//     all 256 keys (lanes = d) and adds it with buffer atomics;
+//   * dS is written to LDS once (transposed, 16-byte writes); dQ of one
+//     query tile is formed during the next: each wave takes one 32-column
+//     slice of dQ over all 256 keys (lanes = d) and adds it with buffer
+//     atomics; query tiles are visited from the last down to the diagonal so
+//     that the workgroups of a (batch, head) add to the same dQ rows at the
+//     same time and the atomics stay in L2;
 //   * one wave per SIMD means the wave itself must keep the matrix core fed:
-//     the products of a tile run in one interleaved stream (S and dP of tile
-//     i with dQ of tile i-1, then dV and dK), operands are read two products
-//     ahead, and the softmax work (P and dS) runs beside the dQ and dV/dK
-//     products instead of between them;
+//     the products of a tile run in one interleaved stream (S and dP, dV and
+//     dK, and dQ of the previously visited tile), operands are read ahead,
+//     and the softmax work (P and dS) runs beside the products instead of
+//     between them;
 //   * rows of the LDS tiles are XOR-swizzled per 16-byte chunk so that both
 //     the 16-row reads and the 4-row transposed reads hit distinct banks.
 #include "fa_device.h"
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // of that copy read past the row range and write zeros behind it. Two
   // waves copy the same L or D bytes to the same place.
   auto issue_qtile = [&](int i) INL {
-    const int qt = qt_begin + i;
+    const int qt = n_qt - 1 - i;
     const bool live = i < nt;
     const unsigned so = rg_a + (i % kStages) * C::STAGE;
 #pragma unroll
@@ -280,20 +283,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS));   // K tile, V operands, query tile 0
   lds_barrier();
 
-  // Query tile i (qt = qt_begin + i) is in ring stage i % 3; its dS^T goes to
-  // dS buffer i % 2, which dQ of tile i reads during tile i + 1.
+  // Query tiles are visited from the last one down to the diagonal: the
+  // workgroups of one (batch, head) then work on the same rows of dQ at the
+  // same time, so its atomics meet in L2 instead of spreading over the whole
+  // accumulator. Visit i (query tile qt = n_qt - 1 - i) is in ring stage
+  // i % 3; its dS^T goes to dS buffer i % 2, which dQ of visit i reads during
+  // visit i + 1.
   for (int i = 0; i < nt; ++i) {
-    const int qt = qt_begin + i;
+    const int qt = n_qt - 1 - i;
     if (i > 0) {
-      // Copies issued after tile i's own: (i >= 2) the 16 atomics of tile
-      // i-2's dQ, then tile i+1 and the 16 atomics of tile i-1's dQ.
+      // Memory operations issued after visit i's own copies: (i >= 2) the 16
+      // dQ atomics of visit i-2, then the copies of visit i+1 and the 16 dQ
+      // atomics of visit i-1.
       if (i == 1)
         __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + 16));
       else
         __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + 32));
       lds_barrier();
     }
-    issue_qtile(i + 2);   // into the stage of tile i-1, free after the barrier
+    issue_qtile(i + 2);   // into the stage of visit i-1, free after the barrier
 
     const int q0 = qt * kBR;
     const unsigned char* qs = ring(i % kStages);
@@ -358,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
     // ---- Phase 2: dV += P^T dO and dK += dS^T Q of key block 0 beside the
     // softmax of key block 1; phase 3: the same products of key block 1 with
-    // dQ of tile i-1 (its dS^T is complete in LDS) interleaved. The B operands
+    // dQ of visit i-1 (its dS^T is complete in LDS) interleaved. The B operands
     // of dV and dK are read transposed from the ring one (ks, db) step ahead
     // (once per key block); the dQ operands one product ahead.
     auto trd = [&](int step) INL {
@@ -417,10 +425,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    dq_atomics(dq_acc, qt - 1, i > 0);
+    dq_atomics(dq_acc, qt + 1, i > 0);
   }
 
-  // dQ of the last tile.
+  // dQ of the last visited tile.
   lds_barrier();
   {
     const unsigned char* sb = dsb((nt - 1) & 1);
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       dq_acc = mma(join(qop[m % 3].v[0], qop[m % 3].v[1]), join(qop[m % 3].v[2], qop[m % 3].v[3]), dq_acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    dq_atomics(dq_acc, qt_begin + nt - 1, true);
+    dq_atomics(dq_acc, qt_begin, true);
   }
 
   // Epilogue: dK = scale * acc, dV = acc (lanes = d, rows = keys); rows past N dropped.
