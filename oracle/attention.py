@@ -153,6 +153,36 @@ def backward_head(q, k, v, do, scale: float, causal: bool, row_chunk: int = 1024
     return dq, dk, dv
 
 
+def backward_from_saved(q, k, v, o, lse, do, scale: float, causal: bool = False):
+    """Gradients of one head (or [B, H, N, d] inputs) from the saved O and L.
+
+    The backward pass as the pages state it ("6.1 FlashAttention V1详解",
+    sections 6.1-6.2): it takes Q, K, V, dO and the forward's saved O and
+    statistics, recomputes P = exp(S - L) from the scores and L, and forms
+    D = rowsum(dO * O) from the given O. With the exact O and L this equals
+    ``backward``; given a rounded O (a bf16 forward's output) it is the exact
+    result of the backward step on that input.
+    """
+    q, k, v, o, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(do)
+    lse = _f64(lse)
+    if q.ndim == 4:
+        out = [np.empty_like(q), np.empty_like(k), np.empty_like(v)]
+        for b in range(q.shape[0]):
+            for h in range(q.shape[1]):
+                g = backward_from_saved(q[b, h], k[b, h], v[b, h], o[b, h], lse[b, h], do[b, h], scale, causal)
+                for t, x in zip(out, g):
+                    t[b, h] = x
+        return tuple(out)
+    s = scores(q, k, scale, causal, 0)
+    with np.errstate(invalid="ignore"):
+        p = np.where(np.isfinite(s), np.exp(s - lse[:, None]), 0.0)   # P = exp(S - L)
+    d_rows = np.sum(do * o, axis=1)                                    # D = rowsum(dO * O)
+    dv = p.T @ do                                                      # dV = P^T dO
+    dp = do @ v.T                                                      # dP = dO V^T
+    ds = p * (dp - d_rows[:, None])                                    # dS = P * (dP - D)
+    return float(scale) * (ds @ k), float(scale) * (ds.T @ q), dv      # dQ, dK, dV
+
+
 def backward(q, k, v, do, scale: float, causal: bool = False, row_chunk: int = 1024):
     """Gradients for [B, H, N, d] (or [N, d]) inputs; see ``backward_head``."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)

@@ -134,3 +134,39 @@ def test_row_chunking_does_not_change_rows():
     g2 = A.backward(q, k, v, do, 0.3, True, row_chunk=1024)
     for a, b in zip(g1, g2):
         assert np.max(np.abs(a - b)) <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_from_saved_pins(causal):
+    """The backward from the saved O and L ("6.1 FlashAttention V1详解", 6.1-6.2).
+
+    * with the exact forward's O and L it is the gradient of ``backward``
+      (itself pinned by finite differences and autograd);
+    * it is linear in O through D only: perturbing O by delta changes dQ by
+      -scale diag(rowsum(dO * delta)) P K and dK by the transpose form, and
+      leaves dV unchanged;
+    * shifting every L by c scales P, hence every gradient, by exp(-c).
+    """
+    rng = np.random.default_rng(77)
+    n, d, scale = 19, 8, 0.4
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    o, lse = A.forward(q, k, v, scale, causal)
+    g_saved = A.backward_from_saved(q, k, v, o, lse, do, scale, causal)
+    g_ref = A.backward(q, k, v, do, scale, causal)
+    for a, b in zip(g_saved, g_ref):
+        assert np.max(np.abs(a - b)) <= 1e-12
+    delta = 1e-3 * rng.standard_normal((n, d))
+    g_pert = A.backward_from_saved(q, k, v, o + delta, lse, do, scale, causal)
+    s = q @ k.T * scale
+    if causal:
+        s = np.where(np.tril(np.ones((n, n), bool)), s, -np.inf)
+    p = np.exp(s - lse[:, None])
+    dd = np.sum(do * delta, axis=1)
+    want_dq = g_saved[0] - scale * (dd[:, None] * p) @ k
+    want_dk = g_saved[1] - scale * (dd[:, None] * p).T @ q
+    assert np.max(np.abs(g_pert[0] - want_dq)) <= 1e-12
+    assert np.max(np.abs(g_pert[1] - want_dk)) <= 1e-12
+    assert np.max(np.abs(g_pert[2] - g_saved[2])) == 0.0
+    g_shift = A.backward_from_saved(q, k, v, o, lse + 0.7, do, scale, causal)
+    for a, b in zip(g_shift, g_saved):
+        assert np.max(np.abs(a - math.exp(-0.7) * b)) <= 1e-12
