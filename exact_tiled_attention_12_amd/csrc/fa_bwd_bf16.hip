@@ -80,7 +80,6 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x2 tr_read(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, p)));
 }
@@ -95,28 +94,6 @@ __device__ __forceinline__ bf16x8 join(u32x2 lo, u32x2 hi) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-
-// The same raw buffer resource as four scalar words, for the LDS-destination
-// copies below.
-__device__ __forceinline__ i32x4 dma_rsrc(const void* base, unsigned bytes) {
-  const unsigned long long b = (unsigned long long)base;
-  return i32x4{__builtin_amdgcn_readfirstlane((int)(unsigned)b),
-               __builtin_amdgcn_readfirstlane((int)((unsigned)(b >> 32) & 0xFFFFu)),
-               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
-}
-
-// 16 bytes per lane from buffer offset `voffset` (past num_records: zeros) to
-// LDS byte address lds_addr + 16 * lane; lds_addr is wave-uniform (M0).
-// Inline assembly, so that the compiler does not count the copy as a pending
-// writer of the ring (it would wait for every copy in flight before any LDS
-// read); the kernel orders the copies itself with vmcnt waits and barriers.
-__device__ __forceinline__ void dma_load16(i32x4 rsrc, unsigned lds_addr, unsigned voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voffset), "s"(rsrc) : "memory", "m0");
-}
-
-// s_waitcnt immediate (gfx9 encoding): vmcnt(n) only (n < 64).
-constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Workgroup barrier ordering LDS only (copies to other ring stages stay in
 // flight; each wave first waits for its own copies of the tile).

@@ -120,6 +120,33 @@ __device__ __forceinline__ void store_bytes(void* dst, const void* src) {
   }
 }
 
+// ---- HBM -> LDS copies (buffer loads with an LDS destination).
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// A raw buffer resource (base, num_records = bytes, no stride) as four scalar
+// words. Offsets at or past `bytes` read as zero.
+__device__ __forceinline__ i32x4 dma_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(unsigned)b),
+               __builtin_amdgcn_readfirstlane((int)((unsigned)(b >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset `voffset` to LDS byte address
+// lds_addr + 16 * lane; lds_addr is wave-uniform and goes in M0. Written as
+// inline assembly so that the compiler does not count the copy as a pending
+// writer of the LDS reads that follow (with the builtin it waits for every
+// copy in flight before them); the kernels order the copies themselves with
+// vmcnt waits and barriers.
+__device__ __forceinline__ void dma_load16(i32x4 rsrc, unsigned lds_addr, unsigned voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voffset), "s"(rsrc) : "memory", "m0");
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n (n < 64) only.
+constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 // Map the hardware workgroup id to a logical id so that consecutive logical
 // ids run on the same XCD: workgroups are dealt to the 8 XCDs round-robin,
 // so hardware id w runs on XCD w % 8. Requires grid % 8 == 0.

@@ -217,7 +217,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;    // query rows per workgroup
 constexpr int kBC = 64;             // keys per tile = rows per scale block
-constexpr int kStages = 3;
+constexpr int kStages = 8;
 constexpr int kD = 128;
 constexpr int kRB = kD;             // bytes per fp8 row
 constexpr int kTile = kBC * kRB;    // 8 KiB
@@ -253,18 +253,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 // operand therefore loads key 32t + 16*((p>>2)&1) + 4*(p>>3) + (p&3).
 __device__ __forceinline__ int pos_to_key(int p) { return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3); }
 
+template <int N_>
+using IC = std::integral_constant<int, N_>;
+#define INL __attribute__((always_inline)) __device__
+
+// Workgroup barrier for the LDS ring, ordering LDS only: each wave first
+// waits (vmcnt) for its own copies of the tile; copies still in flight to
+// other stages stay in flight.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The fp8 attention runs the same software pipeline as the bf16 forward:
+// step j (one 64-key tile) forms the softmax of tile j while the matrix cores
+// run S of tile j+1 and the product of tile j-1 with V; none of the step's 8
+// products depends on its vector work, so they are interleaved one product
+// at a time. The running maximum stays exact per tile (a stale maximum would
+// push 448 P past the e4m3 range). The accumulator is kept in units of the
+// current tile's V scale, so before the product of tile j-1 it is multiplied
+// by alpha_{j-1} sV_{j-2} / sV_{j-1}.
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(1024))) unsigned char st0[kStage];
-  __shared__ __attribute__((aligned(1024))) unsigned char st1[kStage];
-  __shared__ __attribute__((aligned(1024))) unsigned char st2[kStage];
-  auto sp = [&](auto stag) -> unsigned char* {
-    constexpr int S = decltype(stag)::value;
-    if constexpr (S == 0) return st0;
-    else if constexpr (S == 1) return st1;
-    else return st2;
-  };
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStage];
+  auto sp = [&](auto stag) INL -> unsigned char* { return ring + decltype(stag)::value * kStage; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -281,10 +295,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   const size_t base = (size_t)bh * (size_t)N * kD;
   const unsigned head_bytes = (unsigned)N * kRB;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q8 + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k8 + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v8 + base, head_bytes);
-  const float* sk = a.sk + (size_t)bh * nb;
-  const float* sv = a.sv + (size_t)bh * nb;
+  const i32x4 rk = dma_rsrc(a.k8 + base, head_bytes);
+  const i32x4 rv = dma_rsrc(a.v8 + base, head_bytes);
+  // Block scales are read through the constant address space so that they
+  // come in by scalar loads: a vector load would make the compiler wait for
+  // every outstanding copy of the ring before its use.
+  typedef __attribute__((address_space(4))) const float cfloat;
+  const cfloat* sk = (const cfloat*)(a.sk + (size_t)bh * nb);
+  const cfloat* sv = (const cfloat*)(a.sv + (size_t)bh * nb);
 
   const int q0 = qt * kBR;
   const int wrow0 = q0 + wave * 32;
@@ -294,17 +312,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   const int kv_end = CAUSAL ? min(nb, (min(q0 + kBR, N) - 1) / kBC + 1) : nb;
 
-  // Tile loads: wave w fills rows 8w .. 8w+7 of K and of V; lane l writes
+  // Tile copies: wave w fills rows 8w .. 8w+7 of K and of V; lane l writes
   // physical chunk l % 8 of row 8w + l / 8 with the logical chunk the
-  // swizzle maps there.
-  auto issue_tile = [&](int j, auto stag) __device__ {
+  // swizzle maps there. A tile at or past kv_end reads past the buffer
+  // (zeros, no traffic), so every tile has two copies per wave in flight.
+  auto issue_tile = [&](int j, auto stag) INL {
     const int row = wave * 8 + (lane >> 3);
     const int p = lane & 7;
-    const unsigned grow = (unsigned)(j * kBC + row) * kRB;
-    unsigned char* kd = sp(stag) + wave * 1024;
-    unsigned char* vd = kd + kTile;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS(void, kd), 16, grow + 16 * (p ^ k_swz(row)), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS(void, vd), 16, grow + 16 * (p ^ v_swz(row)), 0, 0, 0);
+    const unsigned grow = j < kv_end ? (unsigned)(j * kBC + row) * kRB : 0x80000000u;
+    const unsigned kd = (unsigned)(uintptr_t)LDS(unsigned char, sp(stag)) + wave * 1024;
+    dma_load16(rk, kd, grow + 16 * (p ^ k_swz(row)));
+    dma_load16(rv, kd + kTile, grow + 16 * (p ^ v_swz(row)));
   };
 
   // Q rows of this wave as the B operand of S^T = K Q^T: lane (l32, hh)
@@ -319,8 +337,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // K fragment of lane (l32, hh) for 32-key block t, d step ks, 16-byte half
-  // hb: row 32t + pos_to_key(l32), logical chunk 4ks + 2hh + hb. The swizzle
+  // K fragment of lane (l32, hh) for 32-key block tb, d step ks, 16-byte half
+  // hb: row 32tb + pos_to_key(l32), logical chunk 4ks + 2hh + hb. The swizzle
   // depends on l32 only, and ks / hb flip address bits 6 / 4.
   const int krow = pos_to_key(l32);
   const unsigned k_lane = (unsigned)krow * kRB + 16 * ((2 * hh) ^ k_swz(krow));
@@ -334,13 +352,142 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   float m = -INFINITY;     // running maximum of this lane's row (scaled log2 units)
   float l = 0.f;           // sum of P' = 448 P~ over this lane half's keys
-  float sv_cur = 1.f;      // V scale the accumulator is expressed in
+  float sv_cur = 1.f;      // V scale of the newest tile the accumulator was brought to
+  float gam = 1.f;         // factor that brings the accumulator to the next tile's units
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
 
-  auto qk = [&](auto stag, f32x16 (&s)[2]) __device__ {
-    const unsigned char* kt = sp(stag);
+  // Operands of the step's products. Position p (0..7): even p is S product
+  // (tb, ks) = (p/4, (p/2)%2) of the next tile, odd p the V product mt = p/2
+  // of the previous tile.
+  struct Ops {
+    i32x8 kf[4];
+    i32x8 vf[4];
+  };
+  auto fetch = [&](int p, Ops& o, const unsigned char* kt, const unsigned char* vt) INL {
+    if (p % 2 == 0) {
+      const int tb = p / 4, ks = (p / 2) % 2;
+      const unsigned a0 = (k_lane ^ (64u * ks)) + tb * 32 * kRB;
+      const u32x4 lo = *LDS(u32x4, kt + a0);
+      const u32x4 hi = *LDS(u32x4, kt + (a0 ^ 16u));
+      o.kf[p / 2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    } else {
+      const int mt = p / 2;
+      u32x2 vr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vr[q] = tr8_read(vt + (v_lane ^ (32u * mt)) + 4096 * (q >> 1) + 1024 * (q & 1));
+      o.vf[mt] = i32x8{(int)vr[0][0], (int)vr[0][1], (int)vr[1][0], (int)vr[1][1],
+                       (int)vr[2][0], (int)vr[2][1], (int)vr[3][0], (int)vr[3][1]};
+    }
+  };
+  auto ktile = [&](auto kst) INL -> const unsigned char* { return sp(kst); };
+  auto vtile = [&](auto vst) INL -> const unsigned char* { return sp(vst) + kTile; };
+  constexpr int AHEAD = 3;
+
+  // Scores of tile j past N or (causal) above the diagonal -> -inf; needed on
+  // ragged and diagonal tiles only.
+  auto masked = [&](int j) INL { return j * kBC + kBC > N || (CAUSAL && j * kBC + kBC - 1 > wrow0); };
+  auto apply_mask = [&](int j, f32x16 (&sc)[2]) INL {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j * kBC + 32 * tb + 16 * hh + r;
+        const bool ok = key < N && (!CAUSAL || key <= qrow);
+        sc[tb][r] = ok ? sc[tb][r] : -INFINITY;
+      }
+  };
+
+  // One pipeline step: softmax of tile j (raw scores sc, fp8 P to pc), S of
+  // tile j+1 into sn, and O += V^T P^T of tile j-1 (pp, V operands from the
+  // step's fetches). The accumulator block mt is brought to the units of tile
+  // j-1 (factor gam from the previous step) just before its product.
+  auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], const i32x8& pp, i32x8& pc, Ops& cur, Ops& nxt,
+                  const unsigned char* kt, const unsigned char* vt, const unsigned char* nkt,
+                  const unsigned char* nvt, float skj, float svj_in) INL {
+    if (masked(j)) apply_mask(j, sc);
+    // Tile scales (a drain step past the last tile keeps the current V unit;
+    // its exponentials are all zero, whatever c_j is).
+    const float cj = cq * skj;
+    const float svj = j < kv_end ? svj_in : sv_cur;
+    // Row maximum of the raw scores; c_j > 0, so the scaled maximum is c_j
+    // times it.
+    float mx = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
+    mx = halves_max(mx) * cj;
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    const float gam_prev = gam;
+    gam = alpha * (sv_cur / svj);
+    m = m_new;
+    sv_cur = svj;
+    l *= alpha;
+    // P' = 2^(c_j s - m + log2 448) = 448 P~, four per position.
+    const float nmo = kLog2_448 - m_use;
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    float part[4];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      if (p + AHEAD < 8)
+        fetch(p + AHEAD, cur, kt, vt);
+      else
+        fetch(p + AHEAD - 8, nxt, nkt, nvt);
+      if (p % 2 == 0) {
+        const int tb = p / 4, ks = (p / 2) % 2;
+        acc[tb] = mma_fp8(cur.kf[p / 2], qf[ks], acc[tb]);
+      } else {
+        const int mt = p / 2;
+        oacc[mt] *= gam_prev;
+        oacc[mt] = mma_fp8(cur.vf[mt], pp, oacc[mt]);
+      }
+      // Scores 4p .. 4p+3: word p of the fp8 P operand.
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[i] = fast_exp2(__builtin_fmaf(sc[p >> 2][4 * (p & 3) + i], cj, nmo));
+        part[i] = p == 0 ? e[i] : part[i] + e[i];
+      }
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], word, true);
+      pc[p] = word;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sn[0] = acc[0];
+    sn[1] = acc[1];
+    l += (part[0] + part[1]) + (part[2] + part[3]);
+  };
+
+  // Ring bookkeeping before step j (j >= 1): step j reads K of tiles j+1 and
+  // j+2 and V of tiles j-1 and j, so tile j+2 must be resident while tiles
+  // j+3 .. j+5 stay in flight; tile j-2 was last read by step j-1, so its
+  // stage takes tile j+6.
+  auto tile_sync = [&](int j, auto nst) INL {
+    __builtin_amdgcn_s_waitcnt(wait_vm(6));
+    ring_barrier();
+    issue_tile(j + 6, nst);
+  };
+
+  // Prologue: tiles 0..6 in flight, tiles 0..2 resident; S of tile 0;
+  // step 0 (its product with V is of a zero P against tile 0's V, which is
+  // finite).
+  issue_tile(0, IC<0>{});
+  issue_tile(1, IC<1>{});
+  issue_tile(2, IC<2>{});
+  issue_tile(3, IC<3>{});
+  issue_tile(4, IC<4>{});
+  issue_tile(5, IC<5>{});
+  issue_tile(6, IC<6>{});
+  __builtin_amdgcn_s_waitcnt(wait_vm(8));
+  ring_barrier();
+
+  f32x16 sa[2], sb[2];
+  i32x8 pa, pb = i32x8{};
+  Ops oa, ob;
+  {
+    const unsigned char* kt = ktile(IC<0>{});
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       f32x16 acc = f32x16{};
@@ -349,116 +496,65 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
         const unsigned a0 = (k_lane ^ (64u * ks)) + tb * 32 * kRB;
         const u32x4 lo = *LDS(u32x4, kt + a0);
         const u32x4 hi = *LDS(u32x4, kt + (a0 ^ 16u));
-        const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         acc = mma_fp8(kf, qf[ks], acc);
       }
-      s[tb] = acc;
+      sa[tb] = acc;
     }
-  };
-
-  // Softmax of tile j (scores in s) and O^T += V^T P^T over its 64 keys.
-  // Masking (keys >= N, causal) is applied on ragged and diagonal tiles only.
-  auto softmax_pv = [&](int j, bool mask, f32x16 (&s)[2], auto stag) __device__ {
-    const float cj = cq * sk[j];
-    const float svj = sv[j];
-    if (mask) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j * kBC + 32 * tb + 16 * hh + r;
-          const bool ok = key < N && (!CAUSAL || key <= qrow);
-          s[tb][r] = ok ? s[tb][r] * cj : -INFINITY;
-        }
-    } else {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) s[tb] *= cj;
-    }
-    float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    const float gamma = alpha * (sv_cur / svj);
-    m = m_new;
-    sv_cur = svj;
-    l *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) oacc[mt] *= gamma;
-    // P' = 2^(s - m + log2 448) = 448 P~, converted two values at a time.
-    const float mo = m_use - kLog2_448;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-    i32x8 pf;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      float e[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e[i] = fast_exp2(s[w >> 2][4 * (w & 3) + i] - mo);
-        part[i] += e[i];
-      }
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], word, true);
-      pf[w] = word;
-    }
-    l += (part[0] + part[1]) + (part[2] + part[3]);
-    const unsigned char* vt = sp(stag) + kTile;
-    u32x2 vr[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) vr[mt][q] = tr8_read(vt + (v_lane ^ (32u * mt)) + 4096 * (q >> 1) + 1024 * (q & 1));
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const i32x8 vf = {(int)vr[mt][0][0], (int)vr[mt][0][1], (int)vr[mt][1][0], (int)vr[mt][1][1],
-                        (int)vr[mt][2][0], (int)vr[mt][2][1], (int)vr[mt][3][0], (int)vr[mt][3][1]};
-      oacc[mt] = mma_fp8(vf, pf, oacc[mt]);
-    }
-  };
-
-  // A wave computes tile j only if some of its rows see a key of it.
-  auto active = [&](int j) __device__ { return j < kv_end && (!CAUSAL || j * kBC <= wrow0 + 31); };
-  auto masked = [&](int j) __device__ { return j * kBC + kBC > N || (CAUSAL && j * kBC + kBC - 1 > wrow0); };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-
-  issue_tile(0, I0{});
-  if (kv_end > 1) issue_tile(1, I1{});
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  f32x16 sc[2], sn[2];
-  if (active(0)) qk(I0{}, sc);
-
-  // Tile j in stage j % 3. The barrier makes tile j+1 resident and frees
-  // the stage of tile j-1 for tile j+2; S of tile j+1 is formed while the
-  // softmax of tile j runs.
-  auto tile = [&](int j, auto stag) __device__ {
-    constexpr int S = decltype(stag)::value;
-    using S1 = std::integral_constant<int, (S + 1) % kStages>;
-    using S2 = std::integral_constant<int, (S + 2) % kStages>;
-    if (j > 0) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-    }
-    if (j + 2 < kv_end) issue_tile(j + 2, S2{});
-    if (active(j + 1)) qk(S1{}, sn);
-    __builtin_amdgcn_sched_barrier(0);
-    if (active(j)) softmax_pv(j, masked(j), sc, stag);
-    sc[0] = sn[0];
-    sc[1] = sn[1];
-  };
-  int j = 0;
-  for (; j + kStages <= kv_end; j += kStages) {
-    tile(j, I0{});
-    tile(j + 1, I1{});
-    tile(j + 2, I2{});
   }
-  if (j < kv_end) tile(j, I0{});
-  if (j + 1 < kv_end) tile(j + 1, I1{});
+#pragma unroll
+  for (int p = 0; p < AHEAD; ++p) fetch(p, oa, ktile(IC<1>{}), vtile(IC<0>{}));
+  step(0, sa, sb, pb, pa, oa, ob, ktile(IC<1>{}), vtile(IC<0>{}), ktile(IC<2>{}), vtile(IC<0>{}), sk[0], sv[0]);
+
+  // Scales of tiles j0 .. j0+7 (indices clamped to the last block: past
+  // kv_end they are not used).
+  auto ld_scales = [&](int j0, float (&ks)[kStages], float (&vs)[kStages]) INL {
+#pragma unroll
+    for (int i = 0; i < kStages; ++i) {
+      const int b = min(j0 + i, nb - 1);
+      ks[i] = sk[b];
+      vs[i] = sv[b];
+    }
+  };
+  float skc[kStages], svc[kStages], skn[kStages], svn[kStages];
+  ld_scales(1, skc, svc);
+
+  // Steps 1..kv_end, eight per iteration (ring stages are compile-time). Step
+  // j reads K of tile j+1 (stage (j+1) % 8) and V of tile j-1 (stage
+  // (j-1) % 8). Step kv_end is a drain: its tile is past the last key or
+  // above the diagonal, so the mask zeroes its exponentials, and it completes
+  // the product of tile kv_end-1.
+  auto one = [&](auto s_tag, int j0) INL -> bool {
+    constexpr int S = decltype(s_tag)::value;   // j = j0 + S, j0 = 1 (mod 8)
+    const int j = j0 + S;
+    tile_sync(j, IC<(S + 7) % kStages>{});
+    const unsigned char* kt = ktile(IC<(S + 2) % kStages>{});
+    const unsigned char* vt = vtile(IC<S % kStages>{});
+    const unsigned char* nkt = ktile(IC<(S + 3) % kStages>{});
+    const unsigned char* nvt = vtile(IC<(S + 1) % kStages>{});
+    if constexpr (S % 2 == 0)
+      step(j, sb, sa, pa, pb, ob, oa, kt, vt, nkt, nvt, skc[S], svc[S]);
+    else
+      step(j, sa, sb, pb, pa, oa, ob, kt, vt, nkt, nvt, skc[S], svc[S]);
+    return j == kv_end;
+  };
+  for (int j0 = 1;; j0 += kStages) {
+    ld_scales(j0 + kStages, skn, svn);
+    if (one(IC<0>{}, j0)) break;
+    if (one(IC<1>{}, j0)) break;
+    if (one(IC<2>{}, j0)) break;
+    if (one(IC<3>{}, j0)) break;
+    if (one(IC<4>{}, j0)) break;
+    if (one(IC<5>{}, j0)) break;
+    if (one(IC<6>{}, j0)) break;
+    if (one(IC<7>{}, j0)) break;
+#pragma unroll
+    for (int i = 0; i < kStages; ++i) {
+      skc[i] = skn[i];
+      svc[i] = svn[i];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   // O = acc * sV / l' and LSE = (m + log2 l' - log2 448) ln 2.
   const float lt = halves_sum(l);

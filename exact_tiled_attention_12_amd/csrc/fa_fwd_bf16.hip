@@ -83,9 +83,6 @@ struct Cfg {
   static_assert(2 * LOADS <= 15, "vmcnt immediates below assume waits for at most 15 loads");
 };
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt(n) only (n < 16).
-constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8); }
-
 // Physical chunk of logical chunk c in LDS row r. K: the 16 rows read together
 // by one 16-lane group land on 16 distinct bank groups. V: 4 consecutive rows
 // x 4 consecutive chunks (one ds_read_b64_tr_b16 group) do.
@@ -101,28 +98,6 @@ __device__ __forceinline__ u32x2 tr_read(const unsigned char* lds_byte_ptr) {
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// The same raw buffer resource (base, num_records = bytes, no stride) as four
-// scalar words, for the LDS-destination loads below.
-__device__ __forceinline__ i32x4 dma_rsrc(const void* base, unsigned bytes) {
-  const unsigned long long b = (unsigned long long)base;
-  return i32x4{__builtin_amdgcn_readfirstlane((int)(unsigned)b),
-               __builtin_amdgcn_readfirstlane((int)((unsigned)(b >> 32) & 0xFFFFu)),
-               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
-}
-
-// 16 bytes per lane from buffer offset `voffset` (past num_records: zeros) to
-// LDS byte address lds_addr + 16 * lane; lds_addr is wave-uniform and goes in
-// M0. Written as inline assembly so that the compiler does not count the copy
-// as a pending writer of the ring: it would otherwise wait for every copy in
-// flight before LDS reads of other stages. The kernel orders the copies
-// itself (vmcnt waits and barriers).
-__device__ __forceinline__ void dma_load16(i32x4 rsrc, unsigned lds_addr, unsigned voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voffset), "s"(rsrc) : "memory", "m0");
 }
 
 // Workgroup barrier for the LDS ring, ordering LDS only: each wave first
