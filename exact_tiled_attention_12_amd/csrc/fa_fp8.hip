@@ -59,118 +59,193 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return sign | code;
 }
 
+// Buffer resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // ---------------------------------------------------------------- quantiser
 
 constexpr int kQRows = 64;      // rows per scale block
 constexpr int kQThreads = 256;
+constexpr int kQWaves = kQThreads / 64;
+constexpr int kQGrid = 512;     // persistent workgroups (two per compute unit)
+constexpr float kMinNormal = 1.17549435e-38f;
 
 enum QuantMode { kBlockScale = 0, kAmaxOnly = 1, kGivenScale = 2 };
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// Codes of four values with |q| < 464, packed little-endian. The hardware
+// conversion rounds to nearest even and agrees with e4m3_code on that range
+// (checked on MI355X over every float32 in [440, 480] and 4M random values
+// of the e4m3 range); from 464 up it gives NaN, so callers keep |q| < 464.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
 
-// One workgroup per 64-row block of one (batch, head). Thread t owns rows
-// 8*(t/32) .. +8 and columns CPT*(t%32) .. +CPT of the block.
+// Four codes of y / s. With s a normal float32, s = amax / 448 rounded, so
+// |y / s| <= 448 (1 + 2^-23) and the hardware conversion is exact; a
+// subnormal s (a block of tiny values) takes the saturating encoder.
+__device__ __forceinline__ uint32_t codes4(const float* y, float s, bool fast) {
+  if (fast) return e4m3x4(y[0] / s, y[1] / s, y[2] / s, y[3] / s);
+  return e4m3_code(y[0] / s) | e4m3_code(y[1] / s) << 8 | e4m3_code(y[2] / s) << 16 | e4m3_code(y[3] / s) << 24;
+}
+
+// Persistent workgroups of 4 waves walk the 64-row blocks of all (batch,
+// head) pairs; the next block is loaded into registers while the current one
+// is computed.
+//
+// Without rotation, thread t holds 16-byte chunks t + 256 i of the block
+// (row-major), so loads and code stores are contiguous.
+//
+// With rotation, Y = X R is formed on the bf16 matrix cores as
+// Y^T = R^T X^T: X is exact in bf16 and R is split into three bf16 parts
+// R = R1 + R2 + R3 + E with |E| <= 2^-24 |R| elementwise, all summed into one
+// float32 accumulator. The block goes through LDS (rows swizzled by 16-byte
+// chunk) to form the B operand; the R^T fragments of the wave's 32 output
+// columns stay in registers for the whole launch. Accumulator slot i of lane
+// l then holds row l % 32 of the row tile and columns 8 (i / 4) +
+// 4 (l / 32) + i % 4 of the column tile.
 template <int D, bool ROT, int MODE>
-__global__ __launch_bounds__(kQThreads) void quant_kernel(QuantArgs a, int nb) {
-  constexpr int CPT = D / 32;
+__global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantArgs a, int nb, int total) {
+  constexpr int CH = D / 8;                      // 16-byte chunks per row
+  constexpr int LPT = kQRows * CH / kQThreads;   // 16-byte loads per thread per block
+  constexpr int CT = D / 32;                     // 32-column tiles
+  constexpr int WPC = kQWaves / CT;              // waves per column tile
+  constexpr int RT = 2 / WPC;                    // 32-row tiles per wave
+  constexpr int KC = D / 16;                     // 16-wide k chunks
+  constexpr int NV = ROT ? 16 * RT : 8 * LPT;    // values per thread
   const int tid = threadIdx.x;
-  const int blk = blockIdx.x % nb;
-  const int bh = blockIdx.x / nb;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
   const int N = a.N;
-  const int r0 = blk * kQRows;
-  const int rows = min(kQRows, N - r0);
-  const size_t off = ((size_t)bh * N + r0) * D;
-  const __bf16* x = (const __bf16*)a.x + off;
-  const int cg = tid & 31, rg = tid >> 5;
+  const unsigned head_bytes = (unsigned)N * D * 2;
 
-  float y[8][CPT];
+  __shared__ float red[2][kQWaves];
+  __shared__ __attribute__((aligned(16))) __bf16 xs[ROT ? kQRows * D : 8];
+
+  auto load_block = [&](int g, u32x4 (&r)[LPT]) {
+    const int bh = g / nb, blk = g - bh * nb;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc((const __bf16*)a.x + (size_t)bh * N * D, head_bytes);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int f = tid + kQThreads * i;
+      const unsigned off = ((unsigned)(blk * kQRows + f / CH) * D + 8 * (f % CH)) * 2;
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+  };
+
+  const int ct = wave % CT;
+  const int rt0 = (wave / CT) * RT;
+  bf16x8 r1[ROT ? KC : 1], r2[ROT ? KC : 1], r3[ROT ? KC : 1];
   if constexpr (ROT) {
-    __shared__ float xs[kQRows][D];
-    __shared__ float rs[D][D];
-    for (int i = tid; i < D * D / 4; i += kQThreads) ((f32x4*)&rs[0][0])[i] = ((const f32x4*)a.rot)[i];
-    for (int i = tid; i < kQRows * D / 4; i += kQThreads) {
-      const int r = i / (D / 4), c4 = i % (D / 4);
-      bf16x4 v = {};
-      if (r < rows) v = *(const bf16x4*)(x + (size_t)r * D + 4 * c4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) xs[r][4 * c4 + e] = (float)v[e];
-    }
-    __syncthreads();
+    for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) y[i][c] = 0.f;
-    // y = x * rot in float32, summed over k in increasing order.
-    for (int k = 0; k < D; ++k) {
-      float rv[CPT];
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) rv[c] = rs[k][CPT * cg + c];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float xv = xs[8 * rg + i][k];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) y[i][c] = __builtin_fmaf(xv, rv[c], y[i][c]);
+      for (int e = 0; e < 8; ++e) {
+        const float r = a.rot[(16 * kc + 8 * hh + e) * D + 32 * ct + l32];
+        const __bf16 p1 = (__bf16)r;
+        const float t1 = r - (float)p1;     // exact
+        const __bf16 p2 = (__bf16)t1;
+        const float t2 = t1 - (float)p2;    // exact
+        r1[kc][e] = p1;
+        r2[kc][e] = p2;
+        r3[kc][e] = (__bf16)t2;
       }
-    }
-  } else {
+  }
+
+  u32x4 nx[LPT];
+  int g = blockIdx.x;
+  if (g < total) load_block(g, nx);
+  for (int par = 0; g < total; g += gridDim.x, par ^= 1) {
+    float y[NV];
+    if constexpr (ROT) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * rg + i;
-      if (r < rows) {
-        const __bf16* p = x + (size_t)r * D + CPT * cg;
-        if constexpr (CPT == 4) {
-          const bf16x4 v = *(const bf16x4*)p;
+      for (int i = 0; i < LPT; ++i) {
+        const int f = tid + kQThreads * i;
+        const int row = f / CH, c = f % CH;
+        *(u32x4*)&xs[row * D + 8 * (c ^ (row & (CH - 1)))] = nx[i];
+      }
+      __syncthreads();
+      if (g + (int)gridDim.x < total) load_block(g + gridDim.x, nx);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) y[i][c] = (float)v[c];
-        } else {
-          const bf16x2v v = *(const bf16x2v*)p;
-          y[i][0] = (float)v[0];
-          y[i][1] = (float)v[1];
+      for (int t = 0; t < RT; ++t) {
+        const int row = 32 * (rt0 + t) + l32;
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const bf16x8 b = *(const bf16x8*)&xs[row * D + 8 * ((2 * kc + hh) ^ (row & (CH - 1)))];
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r3[kc], b, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r2[kc], b, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r1[kc], b, acc, 0, 0, 0);
         }
-      } else {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) y[i][c] = 0.f;
+        for (int i = 0; i < 16; ++i) y[16 * t + i] = acc[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, nx[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[8 * i + e] = (float)v[e];
+      }
+      if (g + (int)gridDim.x < total) load_block(g + gridDim.x, nx);
+    }
+
+    const int bh = g / nb, blk = g - bh * nb;
+    float* sc = a.scales + g;
+    float s;
+    if constexpr (MODE == kGivenScale) {
+      s = *sc;
+    } else {
+      float am = 0.f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) am = fmaxf(am, fabsf(y[i]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+      if (lane == 0) red[par][wave] = am;
+      __syncthreads();
+      am = fmaxf(fmaxf(red[par][0], red[par][1]), fmaxf(red[par][2], red[par][3]));
+      if constexpr (MODE == kAmaxOnly) {
+        if (tid == 0) *sc = am;
+        continue;
+      }
+      s = am == 0.f ? 1.f : am / 448.f;   // correctly rounded float32 division
+      if (tid == 0) *sc = s;
+    }
+    if constexpr (ROT) {
+      // Without a reduction barrier (given scale) the LDS block must still be
+      // released before the next iteration overwrites it.
+      if constexpr (MODE == kGivenScale) __syncthreads();
+    }
+
+    const bool fast = s >= kMinNormal;
+    const int rows = min(kQRows, N - blk * kQRows);
+    unsigned char* x8 = a.x8 + ((size_t)bh * N + (size_t)blk * kQRows) * D;
+    if constexpr (ROT) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int row = 32 * (rt0 + t) + l32;
+        if (row < rows) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(uint32_t*)(x8 + (size_t)row * D + 32 * ct + 8 * q + 4 * hh) = codes4(&y[16 * t + 4 * q], s, fast);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int f = tid + kQThreads * i;
+        const int row = f / CH;
+        if (row < rows) {
+          u32x2 w;
+          w[0] = codes4(&y[8 * i], s, fast);
+          w[1] = codes4(&y[8 * i + 4], s, fast);
+          *(u32x2*)(x8 + (size_t)row * D + 8 * (f % CH)) = w;
+        }
       }
     }
-  }
-
-  float s;
-  float* sc = a.scales + (size_t)bh * nb + blk;
-  if constexpr (MODE == kGivenScale) {
-    s = *sc;
-  } else {
-    float am = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) am = fmaxf(am, fabsf(y[i][c]));
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
-    __shared__ float red[kQThreads / 64];
-    if ((tid & 63) == 0) red[tid >> 6] = am;
-    __syncthreads();
-    am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if constexpr (MODE == kAmaxOnly) {
-      if (tid == 0) *sc = am;
-      return;
-    }
-    s = am == 0.f ? 1.f : am / 448.f;   // correctly rounded float32 division
-    if (tid == 0) *sc = s;
-  }
-
-  unsigned char* x8 = a.x8 + off;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * rg + i;
-    if (r >= rows) continue;
-    uint32_t w = 0;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) w |= e4m3_code(y[i][c] / s) << (8 * c);
-    if constexpr (CPT == 4)
-      *(uint32_t*)(x8 + (size_t)r * D + 4 * cg) = w;
-    else
-      *(uint16_t*)(x8 + (size_t)r * D + 2 * cg) = (uint16_t)w;
   }
 }
 
@@ -196,18 +271,19 @@ __global__ __launch_bounds__(kRedThreads) void quant_tensor_scale_kernel(float* 
 template <int D, bool ROT>
 hipError_t launch_quant_d(const QuantArgs& a, int B, int H, hipStream_t st) {
   const int nb = (a.N + kQRows - 1) / kQRows;
-  const int grid = B * H * nb;
+  const int total = B * H * nb;
+  const int grid = min(total, kQGrid);
   if (a.block_rows == 64) {
-    hipLaunchKernelGGL((quant_kernel<D, ROT, kBlockScale>), dim3(grid), dim3(kQThreads), 0, st, a, nb);
+    hipLaunchKernelGGL((quant_kernel<D, ROT, kBlockScale>), dim3(grid), dim3(kQThreads), 0, st, a, nb, total);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((quant_kernel<D, ROT, kAmaxOnly>), dim3(grid), dim3(kQThreads), 0, st, a, nb);
+  hipLaunchKernelGGL((quant_kernel<D, ROT, kAmaxOnly>), dim3(grid), dim3(kQThreads), 0, st, a, nb, total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(quant_tensor_scale_kernel, dim3(1), dim3(kRedThreads), 0, st, a.scales, grid);
+  hipLaunchKernelGGL(quant_tensor_scale_kernel, dim3(1), dim3(kRedThreads), 0, st, a.scales, total);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((quant_kernel<D, ROT, kGivenScale>), dim3(grid), dim3(kQThreads), 0, st, a, nb);
+  hipLaunchKernelGGL((quant_kernel<D, ROT, kGivenScale>), dim3(grid), dim3(kQThreads), 0, st, a, nb, total);
   return hipGetLastError();
 }
 
@@ -244,9 +320,6 @@ __device__ __forceinline__ f32x16 mma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // Accumulator slot r of lane half h in 32-key block t holds key 32t + 16h + r
 // of the tile (the K rows are permuted to make it so). A position p of the A

@@ -118,15 +118,18 @@ FA_API int fa_bwd_f32(const float* q, const float* k, const float* v, const floa
 
 /* fp8 quantisation ("FlashAttention v1～v4 完整进化史", v3 part 3).
  * x: [B,H,N,d] bf16. rot: d x d float32 row-major orthogonal matrix or NULL;
- * with rot the quantised tensor is x * rot (float32 products and sums).
+ * with rot the quantised tensor is x * rot, formed on the bf16 matrix cores
+ * with rot split into three bf16 parts (x is exact in bf16) and float32
+ * accumulation; its error stays below the float32 FMA-chain bound
+ * d 2^-24 / (1 - d 2^-24) (|x| |rot|).
  * block_rows = 64: one scale per 64 rows x d of each (b,h);
  * block_rows = 0: one scale for the whole tensor (the per-tensor baseline).
  * scales: [B,H,ceil(N/64)] float32 (written; with block_rows = 0 every entry
  * holds the same value). s = amax / 448 in float32 (1 for an all-zero block);
  * x8 = e4m3fn(x / s) with x / s a correctly rounded float32 division,
  * rounded to nearest even after saturating to +-448 (x8: [B,H,N,d] bytes,
- * written). Inputs are expected finite: a NaN element gets the NaN code 0x7F
- * and is left out of its block's amax.
+ * written). Inputs are expected finite: a NaN element gets a NaN code
+ * (0x7F or 0xFF) and is left out of its block's amax.
  * block_rows = 0 runs three launches and uses scales as scratch between
  * them (every entry ends up holding the one scale). */
 FA_API int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, float* scales,
