@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 workload timing")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="time only the fp8 workload and print its figures as one JSON line")
     ap.add_argument("--cpu-heads", type=int, default=1)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the warm-up, copy MIB MiB device-to-device once (a transfer of known "
@@ -164,6 +166,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     fa.load()
+    if args.fp8_only:
+        print(json.dumps({"fp8": fp8_section(fa, args.steps, args.warmup)}), flush=True)
+        return
     w = si.workload(4)
     B, H, N, d = w.B, w.H, w.N, w.d
     x = si.make_inputs(w)

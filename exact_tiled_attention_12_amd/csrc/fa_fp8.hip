@@ -15,18 +15,19 @@
 //   * one workgroup = 8 waves = 256 query rows; each wave owns 32 rows, which
 //     lie inside one 64-row scale block; key tiles of 64 keys coincide with
 //     the scale blocks of K and V;
-//   * K and V tiles move from HBM into a 3-stage LDS ring with buffer loads
-//     that write LDS directly, two tiles ahead of use;
+//   * K and V tiles move from HBM into an 8-stage LDS ring with buffer loads
+//     that write LDS directly, up to six tiles ahead of use;
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x64_f8f6f4. K rows are
 //     read in a permuted order so that each lane's 32 scores of its query are
 //     exactly the 32 bytes of the P^T operand; V stays row-major and is read
 //     with ds_read_b64_tr_b8;
 //   * the scores are scaled by scale * log2(e) * sQ * sK_j in one FMA that
-//     also folds in the factor 448, so P' = 448 P~ comes out of exp2 ready to
-//     convert; l sums the float32 P' (the factor 448 cancels in O = acc / l);
-//   * the V block scale differs per tile, so the accumulator is kept in units
-//     of the current tile's scale: before tile j's product it is multiplied by
-//     alpha_j * sV_{j-1} / sV_j, and O = acc * sV_last / l at the end.
+//     also folds in the factor 448 r_j, r_j = sV_j / (largest sV so far), so
+//     P' = 448 P~ r_j <= 448 comes out of exp2 ready to convert; l sums
+//     448 P~ (the factor 448 cancels in O = acc / l);
+//   * the accumulator is kept in units of the largest V block scale so far
+//     and is rescaled only when that scale or some row maximum of the wave
+//     grows; O = acc * sV_max / l at the end.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -326,6 +327,21 @@ __device__ __forceinline__ f32x16 mma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 // operand therefore loads key 32t + 16*((p>>2)&1) + 4*(p>>3) + (p&3).
 __device__ __forceinline__ int pos_to_key(int p) { return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3); }
 
+// Maximum of three scores (finite or -inf) as one v_maximum3_f32: fmaxf
+// would first quiet each matrix-core result against signalling NaNs, one
+// extra instruction per score.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+}
+
+// Materialises x at this point of the instruction stream: values produced in
+// one pipeline step for the next must not be sunk into the next step, where
+// nothing would overlap them.
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 template <int N_>
 using IC = std::integral_constant<int, N_>;
 #define INL __attribute__((always_inline)) __device__
@@ -424,29 +440,32 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   const unsigned v_lane = (unsigned)vrow * kRB + 16 * ((g16 & 1) ^ v_swz(vrow)) + 8 * (j16 & 1);
 
   float m = -INFINITY;     // running maximum of this lane's row (scaled log2 units)
-  float l = 0.f;           // sum of P' = 448 P~ over this lane half's keys
-  float sv_cur = 1.f;      // V scale of the newest tile the accumulator was brought to
-  float gam = 1.f;         // factor that brings the accumulator to the next tile's units
+  float l = 0.f;           // sum of 448 P~ over this lane half's keys
+  float svr = 0.f;         // largest V block scale so far (the accumulator's unit)
+  float lsr = -INFINITY;   // its log2
+  float gam = 1.f;         // factor that brings the accumulator to the next step's units
+  bool resc = false;       // some row of the wave has gam != 1
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
 
-  // Operands of the step's products. Position p (0..7): even p is S product
-  // (tb, ks) = (p/4, (p/2)%2) of the next tile, odd p the V product mt = p/2
-  // of the previous tile.
+  // Operands of the step's products. Positions 0..3 are the S products
+  // (tb, ks) = (p/2, p%2) of the next tile, positions 4..7 the V products
+  // mt = p-4 of the previous tile: S comes first so that its row maximum can
+  // be formed inside the step, off the next step's critical path.
   struct Ops {
     i32x8 kf[4];
     i32x8 vf[4];
   };
   auto fetch = [&](int p, Ops& o, const unsigned char* kt, const unsigned char* vt) INL {
-    if (p % 2 == 0) {
-      const int tb = p / 4, ks = (p / 2) % 2;
+    if (p < 4) {
+      const int tb = p / 2, ks = p % 2;
       const unsigned a0 = (k_lane ^ (64u * ks)) + tb * 32 * kRB;
       const u32x4 lo = *LDS(u32x4, kt + a0);
       const u32x4 hi = *LDS(u32x4, kt + (a0 ^ 16u));
-      o.kf[p / 2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      o.kf[p] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     } else {
-      const int mt = p / 2;
+      const int mt = p - 4;
       u32x2 vr[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) vr[q] = tr8_read(vt + (v_lane ^ (32u * mt)) + 4096 * (q >> 1) + 1024 * (q & 1));
@@ -472,48 +491,68 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       }
   };
 
+  // Raw row maximum over the 64 scores of one tile (both lane halves).
+  auto half_max = [&](const f32x16& x) INL -> float {
+    const float a0 = max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8]));
+    return max3(a0, max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]));
+  };
+  auto row_max = [&](const f32x16 (&x)[2]) INL -> float {
+    return halves_max(max3(half_max(x[0]), half_max(x[1]), fmaxf(x[0][15], x[1][15])));
+  };
+
   // One pipeline step: softmax of tile j (raw scores sc, fp8 P to pc), S of
   // tile j+1 into sn, and O += V^T P^T of tile j-1 (pp, V operands from the
-  // step's fetches). The accumulator block mt is brought to the units of tile
-  // j-1 (factor gam from the previous step) just before its product.
+  // step's fetches). mxr holds the raw row maximum of sc on entry (of the
+  // unmasked scores) and that of sn on exit.
+  //
+  // The accumulator is kept in units of the largest V block scale seen so
+  // far, svr: tile j's P' carries the factor r_j = sV_j / svr (<= 1), folded
+  // into the exponent, so P' = 448 P~ r_j <= 448. It then changes units only
+  // when the row maximum or svr grows, and is rescaled (factor gam, from the
+  // previous step) only when that happened for some row of the wave.
   auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], const i32x8& pp, i32x8& pc, Ops& cur, Ops& nxt,
                   const unsigned char* kt, const unsigned char* vt, const unsigned char* nkt,
-                  const unsigned char* nvt, float skj, float svj_in) INL {
-    if (masked(j)) apply_mask(j, sc);
-    // Tile scales (a drain step past the last tile keeps the current V unit;
-    // its exponentials are all zero, whatever c_j is).
+                  const unsigned char* nvt, float skj, float svj_in, float& mxr) INL {
+    if (masked(j)) {
+      apply_mask(j, sc);
+      mxr = row_max(sc);
+    }
+    // Tile scales (a drain step past the last tile keeps the V unit; its
+    // exponentials are all zero, whatever c_j is). c_j > 0, so the scaled
+    // maximum is c_j times the raw one.
+    const bool real = j < kv_end;
     const float cj = cq * skj;
-    const float svj = j < kv_end ? svj_in : sv_cur;
-    // Row maximum of the raw scores; c_j > 0, so the scaled maximum is c_j
-    // times it.
-    float mx = fmaxf(sc[0][0], sc[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
-    mx = halves_max(mx) * cj;
-    const float m_new = fmaxf(m, mx);
+    const float lsv = real ? fast_log2(svj_in) : lsr;
+    const float lsr_new = fmaxf(lsr, lsv);
+    const float lr = lsv - lsr_new;             // log2 r_j
+    const float m_new = fmaxf(m, mxr * cj);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
     const float gam_prev = gam;
-    gam = alpha * (sv_cur / svj);
+    const bool resc_prev = resc;
     m = m_new;
-    sv_cur = svj;
     l *= alpha;
-    // P' = 2^(c_j s - m + log2 448) = 448 P~, four per position.
-    const float nmo = kLog2_448 - m_use;
+    // P' = 2^(c_j s - m + log2 448 + log2 r_j) = 448 P~ r_j, four per position.
+    const float nmo = kLog2_448 + lr - m_use;
     f32x16 acc[2] = {f32x16{}, f32x16{}};
     float part[4];
+    float hm0 = 0.f, hm1 = 0.f;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       if (p + AHEAD < 8)
         fetch(p + AHEAD, cur, kt, vt);
       else
         fetch(p + AHEAD - 8, nxt, nkt, nvt);
-      if (p % 2 == 0) {
-        const int tb = p / 4, ks = (p / 2) % 2;
-        acc[tb] = mma_fp8(cur.kf[p / 2], qf[ks], acc[tb]);
+      if (p < 4) {
+        const int tb = p / 2, ks = p % 2;
+        acc[tb] = mma_fp8(cur.kf[p], qf[ks], acc[tb]);
+        if (resc_prev) {
+          // (kept a branch: as a select it would cost the multiplies anyway)
+          asm volatile("");
+          oacc[p] *= gam_prev;
+        }
       } else {
-        const int mt = p / 2;
-        oacc[mt] *= gam_prev;
+        const int mt = p - 4;
         oacc[mt] = mma_fp8(cur.vf[mt], pp, oacc[mt]);
       }
       // Scores 4p .. 4p+3: word p of the fp8 P operand.
@@ -525,12 +564,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       }
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], word, true);
+      pin(word);
       pc[p] = word;
+      // Uniform bookkeeping, and the next tile's row maximum once its S
+      // products (positions 0..3) have completed.
+      if (p == 0) {
+        gam = alpha * fast_exp2(lsr - lsr_new);
+        resc = __builtin_amdgcn_ballot_w64(gam != 1.f) != 0;
+        pin(gam);
+        lsr = lsr_new;
+        svr = real ? fmaxf(svr, svj_in) : svr;
+      }
+      if (p == 5) hm0 = half_max(acc[0]);
+      if (p == 6) hm1 = half_max(acc[1]);
+      if (p == 7) mxr = halves_max(max3(hm0, hm1, fmaxf(acc[0][15], acc[1][15])));
       __builtin_amdgcn_sched_barrier(0);
     }
     sn[0] = acc[0];
     sn[1] = acc[1];
-    l += (part[0] + part[1]) + (part[2] + part[3]);
+    l = __builtin_fmaf((part[0] + part[1]) + (part[2] + part[3]), fast_exp2(-lr), l);
   };
 
   // Ring bookkeeping before step j (j >= 1): step j reads K of tiles j+1 and
@@ -575,9 +627,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       sa[tb] = acc;
     }
   }
+  float mxr = row_max(sa);
 #pragma unroll
   for (int p = 0; p < AHEAD; ++p) fetch(p, oa, ktile(IC<1>{}), vtile(IC<0>{}));
-  step(0, sa, sb, pb, pa, oa, ob, ktile(IC<1>{}), vtile(IC<0>{}), ktile(IC<2>{}), vtile(IC<0>{}), sk[0], sv[0]);
+  step(0, sa, sb, pb, pa, oa, ob, ktile(IC<1>{}), vtile(IC<0>{}), ktile(IC<2>{}), vtile(IC<0>{}), sk[0], sv[0], mxr);
 
   // Scales of tiles j0 .. j0+7 (indices clamped to the last block: past
   // kv_end they are not used).
@@ -606,9 +659,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     const unsigned char* nkt = ktile(IC<(S + 3) % kStages>{});
     const unsigned char* nvt = vtile(IC<(S + 1) % kStages>{});
     if constexpr (S % 2 == 0)
-      step(j, sb, sa, pa, pb, ob, oa, kt, vt, nkt, nvt, skc[S], svc[S]);
+      step(j, sb, sa, pa, pb, ob, oa, kt, vt, nkt, nvt, skc[S], svc[S], mxr);
     else
-      step(j, sa, sb, pb, pa, oa, ob, kt, vt, nkt, nvt, skc[S], svc[S]);
+      step(j, sa, sb, pb, pa, oa, ob, kt, vt, nkt, nvt, skc[S], svc[S], mxr);
     return j == kv_end;
   };
   for (int j0 = 1;; j0 += kStages) {
@@ -631,7 +684,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   // O = acc * sV / l' and LSE = (m + log2 l' - log2 448) ln 2.
   const float lt = halves_sum(l);
-  const float inv = lt == 0.f ? 0.f : sv_cur / lt;
+  const float inv = lt == 0.f ? 0.f : svr / lt;
   if (qrow < N) {
     __bf16* og = (__bf16*)a.o + base + (size_t)qrow * kD;
 #pragma unroll

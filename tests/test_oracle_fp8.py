@@ -120,19 +120,62 @@ def test_fp8_emulation_without_p_rounding_is_exact_attention():
 
 
 def test_fp8_emulation_p_rounding_within_bound():
-    """Rounding P~ * 448 to e4m3 moves each weight by at most half a step.
+    """Rounding 448 P~ r to e4m3 moves each weight by at most half a step.
 
-    |P8 - P~| <= 2^-4 P~ + 2^-10 / 448 per weight, so each O element moves by
-    at most (2^-4 + 2^-10 / 448 * n_keys / l) * max|v| (ratios with l >= 1).
+    With r = sV_j / (largest V scale so far) <= 1 the e4m3 argument is
+    448 P~ r <= 448, so |P8 - P~| <= 2^-4 P~ + 2^-10 / (448 r) per weight and
+    each O element moves by at most (2^-4 + 2^-10 n_keys / (448 r_min l)) max|v|.
+    The V rows are scaled per block so that r really varies (down to about 1/6).
     """
     rng = np.random.default_rng(35)
     x = {n: rng.standard_normal((1, 1, 192, 16)) for n in "qkv"}
+    x["v"] *= np.repeat(np.array([1.0, 6.0, 0.5]), 64)[None, None, :, None]
     qc = {n: F.quantize(x[n], 64) for n in "qkv"}
     args = (qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1], qc["v"][0], qc["v"][1], 0.25, False)
     o8, l8 = F.fp8_attention_tiled(*args, B_c=64, quantize_p=True)
     o, l = F.fp8_attention_tiled(*args, B_c=64, quantize_p=False)
+    sv = qc["v"][1][0, 0].astype(np.float64)
+    r_min = min(sv[j] / sv[: j + 1].max() for j in range(3))
+    assert r_min < 0.2
     vmax = np.abs(F.dequantize(qc["v"][0], qc["v"][1], 64)).max()
-    bound = (2.0 ** -4 + 2.0 ** -10 / 448 * 192) * vmax
+    bound = (2.0 ** -4 + 2.0 ** -10 / (448 * r_min) * 192) * vmax
     assert np.max(np.abs(o8 - o)) <= bound
     assert np.max(np.abs(o8 - o)) > 0          # the rounding is really applied
     assert np.array_equal(l8, l)                # l comes from the unrounded P~
+
+
+def test_fp8_emulation_v_scale_power_of_two_invariance():
+    """Multiplying every V block scale by 2^k (same codes) multiplies O by 2^k exactly.
+
+    The ratios r_j = sV_j / max sV are unchanged, so every e4m3 code of P is
+    the same and only the dequantised V is scaled.
+    """
+    rng = np.random.default_rng(36)
+    x = {n: rng.standard_normal((1, 2, 150, 8)) for n in "qkv"}
+    x["v"][:, :, 64:128] *= 0.1
+    qc = {n: F.quantize(x[n], 64) for n in "qkv"}
+    for causal in (False, True):
+        base = (qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1], qc["v"][0])
+        o1, l1 = F.fp8_attention_tiled(*base, qc["v"][1], 0.3, causal)
+        o2, l2 = F.fp8_attention_tiled(*base, qc["v"][1] * np.float32(8.0), 0.3, causal)
+        assert np.array_equal(o2, 8.0 * o1)
+        assert np.array_equal(l2, l1)
+
+
+def test_bound_helper_rebuilds_the_emulation():
+    """tests/fp8_bounds.py rebuilds the emulation's O from its own weights; both must agree."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from fp8_bounds import bound_rows
+    rng = np.random.default_rng(37)
+    x = {n: rng.standard_normal((1, 1, 200, 16)) for n in "qkv"}
+    x["v"] *= np.repeat(np.array([1.0, 4.0, 0.3, 2.0]), 64)[None, None, :200, None]
+    qc = {n: F.quantize(x[n], 64) for n in "qkv"}
+    for causal in (False, True):
+        o, lse = F.fp8_attention_tiled(qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1],
+                                       qc["v"][0], qc["v"][1], 0.25, causal)
+        rows = np.arange(200)
+        _, _, o_em, l_em = bound_rows(qc["q"][0][0, 0], qc["q"][1][0, 0], qc["k"][0][0, 0], qc["k"][1][0, 0],
+                                      qc["v"][0][0, 0], qc["v"][1][0, 0], 0.25, causal, rows)
+        assert np.max(np.abs(o_em - o[0, 0])) <= 1e-12
+        assert np.max(np.abs(l_em - lse[0, 0])) <= 1e-12
