@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_tiled_attention_12_amd", "csrc")
 
@@ -131,8 +132,14 @@ def fp8_section(fa, steps: int, warmup: int):
     q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     f_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     tf = attention_flops(B, H, N, d, False) / (f_ms * 1e-3) / 1e12
+    # Quantiser: algorithmic HBM bytes of the three launches (2 B read and 1 B
+    # written per element, plus the block scales).
+    q_bytes = 3 * (B * H * N * d * 3 + B * H * (-(-N // 64)) * 4)
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
     return {"workload": "fp8 e4m3 attention, B=4 H=32 N=8192 d=128, non-causal, block scales + rotation",
-            "quant_ms": round(q_ms, 4), "fwd_ms": round(f_ms, 4), "fwd_tflops": round(tf, 2),
+            "quant_ms": round(q_ms, 4), "quant_gbps": round(q_gbs, 1),
+            "quant_frac_of_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4),
+            "fwd_ms": round(f_ms, 4), "fwd_tflops": round(tf, 2),
             "fwd_frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
 
 
