@@ -22,12 +22,11 @@
 //     exactly the 32 bytes of the P^T operand; V stays row-major and is read
 //     with ds_read_b64_tr_b8;
 //   * the scores are scaled by scale * log2(e) * sQ * sK_j in one FMA that
-//     also folds in the factor 448 r_j, r_j = sV_j / (largest sV so far), so
-//     P' = 448 P~ r_j <= 448 comes out of exp2 ready to convert; l sums
-//     448 P~ (the factor 448 cancels in O = acc / l);
-//   * the accumulator is kept in units of the largest V block scale so far
-//     and is rescaled only when that scale or some row maximum of the wave
-//     grows; O = acc * sV_max / l at the end.
+//     also folds in the factor 448, so P' = 448 P~ comes out of exp2 ready to
+//     convert; l sums the float32 P' (the factor 448 cancels in O = acc / l);
+//   * the V block scale differs per tile, so the accumulator is kept in units
+//     of the current tile's scale: before tile j's product it is multiplied by
+//     alpha_j * sV_{j-1} / sV_j, and O = acc * sV_last / l at the end.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -440,11 +439,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   const unsigned v_lane = (unsigned)vrow * kRB + 16 * ((g16 & 1) ^ v_swz(vrow)) + 8 * (j16 & 1);
 
   float m = -INFINITY;     // running maximum of this lane's row (scaled log2 units)
-  float l = 0.f;           // sum of 448 P~ over this lane half's keys
-  float svr = 0.f;         // largest V block scale so far (the accumulator's unit)
-  float lsr = -INFINITY;   // its log2
-  float gam = 1.f;         // factor that brings the accumulator to the next step's units
-  bool resc = false;       // some row of the wave has gam != 1
+  float l = 0.f;           // sum of P' = 448 P~ over this lane half's keys
+  float sv_cur = 1.f;      // V scale of the newest tile the accumulator was brought to
+  float gam = 1.f;         // factor that brings the accumulator to the next tile's units
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
@@ -502,14 +499,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   // One pipeline step: softmax of tile j (raw scores sc, fp8 P to pc), S of
   // tile j+1 into sn, and O += V^T P^T of tile j-1 (pp, V operands from the
-  // step's fetches). mxr holds the raw row maximum of sc on entry (of the
-  // unmasked scores) and that of sn on exit.
-  //
-  // The accumulator is kept in units of the largest V block scale seen so
-  // far, svr: tile j's P' carries the factor r_j = sV_j / svr (<= 1), folded
-  // into the exponent, so P' = 448 P~ r_j <= 448. It then changes units only
-  // when the row maximum or svr grows, and is rescaled (factor gam, from the
-  // previous step) only when that happened for some row of the wave.
+  // step's fetches). Accumulator block mt is brought to the units of tile
+  // j-1 (factor gam from the previous step) at position mt, before its
+  // product at position 4 + mt. mxr holds the raw row maximum of sc on entry
+  // (of the unmasked scores) and that of sn on exit.
   auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], const i32x8& pp, i32x8& pc, Ops& cur, Ops& nxt,
                   const unsigned char* kt, const unsigned char* vt, const unsigned char* nkt,
                   const unsigned char* nvt, float skj, float svj_in, float& mxr) INL {
@@ -520,20 +513,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     // Tile scales (a drain step past the last tile keeps the V unit; its
     // exponentials are all zero, whatever c_j is). c_j > 0, so the scaled
     // maximum is c_j times the raw one.
-    const bool real = j < kv_end;
     const float cj = cq * skj;
-    const float lsv = real ? fast_log2(svj_in) : lsr;
-    const float lsr_new = fmaxf(lsr, lsv);
-    const float lr = lsv - lsr_new;             // log2 r_j
+    const float svj = j < kv_end ? svj_in : sv_cur;
     const float m_new = fmaxf(m, mxr * cj);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
     const float gam_prev = gam;
-    const bool resc_prev = resc;
     m = m_new;
     l *= alpha;
-    // P' = 2^(c_j s - m + log2 448 + log2 r_j) = 448 P~ r_j, four per position.
-    const float nmo = kLog2_448 + lr - m_use;
+    // P' = 2^(c_j s - m + log2 448) = 448 P~, four per position.
+    const float nmo = kLog2_448 - m_use;
     f32x16 acc[2] = {f32x16{}, f32x16{}};
     float part[4];
     float hm0 = 0.f, hm1 = 0.f;
@@ -546,11 +535,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       if (p < 4) {
         const int tb = p / 2, ks = p % 2;
         acc[tb] = mma_fp8(cur.kf[p], qf[ks], acc[tb]);
-        if (resc_prev) {
-          // (kept a branch: as a select it would cost the multiplies anyway)
-          asm volatile("");
-          oacc[p] *= gam_prev;
-        }
+        oacc[p] *= gam_prev;
       } else {
         const int mt = p - 4;
         oacc[mt] = mma_fp8(cur.vf[mt], pp, oacc[mt]);
@@ -569,11 +554,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       // Uniform bookkeeping, and the next tile's row maximum once its S
       // products (positions 0..3) have completed.
       if (p == 0) {
-        gam = alpha * fast_exp2(lsr - lsr_new);
-        resc = __builtin_amdgcn_ballot_w64(gam != 1.f) != 0;
+        gam = alpha * (sv_cur * __builtin_amdgcn_rcpf(svj));
         pin(gam);
-        lsr = lsr_new;
-        svr = real ? fmaxf(svr, svj_in) : svr;
+        sv_cur = svj;
       }
       if (p == 5) hm0 = half_max(acc[0]);
       if (p == 6) hm1 = half_max(acc[1]);
@@ -582,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     }
     sn[0] = acc[0];
     sn[1] = acc[1];
-    l = __builtin_fmaf((part[0] + part[1]) + (part[2] + part[3]), fast_exp2(-lr), l);
+    l += (part[0] + part[1]) + (part[2] + part[3]);
   };
 
   // Ring bookkeeping before step j (j >= 1): step j reads K of tiles j+1 and
@@ -684,7 +667,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   // O = acc * sV / l' and LSE = (m + log2 l' - log2 448) ln 2.
   const float lt = halves_sum(l);
-  const float inv = lt == 0.f ? 0.f : svr / lt;
+  const float inv = lt == 0.f ? 0.f : sv_cur / lt;
   if (qrow < N) {
     __bf16* og = (__bf16*)a.o + base + (size_t)qrow * kD;
 #pragma unroll

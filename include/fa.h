@@ -140,10 +140,10 @@ FA_API int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, floa
  * value of a code is decode(code) * s of its 64-row block). Keys are taken
  * in tiles of 64 (one scale block each); m is the exact running maximum
  * after each tile, P~ = exp(S - m) <= 1 is rounded to e4m3 as
- * e4m3(448 P~ r_j) for the product with V, with r_j = sv of the tile over
- * the largest sv of the tiles so far (<= 1), and the row sum l uses the
- * float32 P~. Both products run on fp8 matrix cores into float32
- * accumulators. Scales must be positive and finite.
+ * e4m3(P~ * 448) for the product with V (dequantised by sv / 448 of its
+ * tile), and the row sum l uses the float32 P~. Both products run on fp8
+ * matrix cores into float32 accumulators. Scales must be positive and
+ * finite.
  * o: [B,H,N,d] bf16 (written). lse: [B,H,N] float32 (written). d must be
  * 128. */
 FA_API int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* v8,

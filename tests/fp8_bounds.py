@@ -9,16 +9,12 @@ same steps on the same codes; they differ only in how the scores are formed:
     (d = 128), so the bound uses min(EPS_SUM * sum|p|, 2 * EPS_MAX * max|p|)
     with EPS_SUM = 2^-11 and EPS_MAX = 2^-10 (about 2.3x and 3x the
     measurements);
-  * the float32 scaling, exp2 and max steps add a few float32 roundings;
-  * the GPU folds r_j = sV_j / (largest V scale so far) into the exp2
-    argument as log2 sV_j - log2 max sV (hardware log2, about one unit in
-    the last place each), which moves P' by a few float32 roundings of those
-    logarithms; the bound adds them to the score error.
+  * the float32 scaling, exp2 and max steps add a few float32 roundings.
 From a score error |dS_ij| <= delta_ij the bound follows the emulation's own
 steps:
   * the running maximum after each tile moves by at most delta_i = max_j
     delta_ij;
-  * P' = 448 exp(S - m) r therefore moves by a factor of at most
+  * P' = 448 exp(S - m) therefore moves by a factor of at most
     exp(eta_i), eta_i = 2 delta_i;
   * its e4m3 code can be any code between those of P' exp(-eta_i) and
     P' exp(eta_i);
@@ -71,19 +67,12 @@ def bound_rows(q8, sq, k8, sk, v8, sv, scale, causal, rows, B_c=64):
     # score error: matrix-core accumulation + float32 scaling / exp2 arguments
     s_fin = np.where(vis, s, 0.0)
     mma = np.minimum(EPS_MMA * sabs, 2 * EPS_MAX * pmax)
-    # V scale of each key over the largest V scale of the tiles up to its own
-    t_c = -(-N // B_c)
-    tile_of = keys // B_c
-    sv64 = np.asarray(sv, dtype=np.float64)
-    sv_key = sv64[keys // 64]
-    sv_tile_max = np.array([sv_key[t * B_c:(t + 1) * B_c].max() for t in range(t_c)])
-    sv_run = np.maximum.accumulate(sv_tile_max)[tile_of]
-    r = sv_key / sv_run
-    log_err = 8 * U32 * (np.abs(np.log2(sv_key)) + np.abs(np.log2(sv_run)) + 1.0)
-    delta = np.where(vis, mma + 8 * U32 * (np.abs(s_fin) + 1.0) + log_err[None, :], 0.0)
+    delta = np.where(vis, mma + 8 * U32 * (np.abs(s_fin) + 1.0), 0.0)
     dmax = delta.max(axis=1)
     eta = 2.0 * dmax
     # running maximum after each tile of B_c keys
+    t_c = -(-N // B_c)
+    tile_of = keys // B_c
     tmax = np.stack([s[:, t * B_c:(t + 1) * B_c].max(axis=1) for t in range(t_c)], axis=1)
     m_run = np.maximum.accumulate(tmax, axis=1)
     m_fin = m_run[:, -1]
@@ -92,17 +81,16 @@ def bound_rows(q8, sq, k8, sk, v8, sv, scale, causal, rows, B_c=64):
         p = np.where(vis, np.exp(s - m_at), 0.0)     # P~ of the emulation
         w = np.where(vis, np.exp(m_at - m_fin[:, None]), 0.0)
     l = (p * w).sum(axis=1)
-    pr = 448.0 * r[None, :]
-    pq = F.e4m3_decode(F.e4m3_encode((p * pr).astype(np.float32)))
+    pq = F.e4m3_decode(F.e4m3_encode(p.astype(np.float32) * np.float32(448.0)))
     e = np.exp(eta)[:, None]
-    lo = F.e4m3_decode(F.e4m3_encode(np.minimum(p * pr / e, 448.0)))
-    hi = F.e4m3_decode(F.e4m3_encode(np.minimum(p * pr * e, 448.0)))
-    # weights of V_j in O: pq/(448 r) * w / l; GPU: within the code range, with
+    lo = F.e4m3_decode(F.e4m3_encode(np.minimum(p * 448.0 / e, 448.0)))
+    hi = F.e4m3_decode(F.e4m3_encode(np.minimum(p * 448.0 * e, 448.0)))
+    # weights of V_j in O: pq/448 * w / l; GPU: within the code range, with
     # the rescale factors and l each off by at most exp(eta) (plus summation)
     lsum = np.exp(eta + N * U32 * 4)[:, None]
-    a = pq / pr * w / l[:, None]
-    a_hi = hi / pr * w * e * lsum / l[:, None]
-    a_lo = lo / pr * w / (e * lsum) / l[:, None]
+    a = pq / 448.0 * w / l[:, None]
+    a_hi = hi / 448.0 * w * e * lsum / l[:, None]
+    a_lo = lo / 448.0 * w / (e * lsum) / l[:, None]
     da = np.maximum(a_hi - a, a - a_lo)
     vabs = np.abs(vd)
     o_emul = a @ vd

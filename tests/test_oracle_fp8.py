@@ -120,12 +120,11 @@ def test_fp8_emulation_without_p_rounding_is_exact_attention():
 
 
 def test_fp8_emulation_p_rounding_within_bound():
-    """Rounding 448 P~ r to e4m3 moves each weight by at most half a step.
+    """Rounding P~ * 448 to e4m3 moves each weight by at most half a step.
 
-    With r = sV_j / (largest V scale so far) <= 1 the e4m3 argument is
-    448 P~ r <= 448, so |P8 - P~| <= 2^-4 P~ + 2^-10 / (448 r) per weight and
-    each O element moves by at most (2^-4 + 2^-10 n_keys / (448 r_min l)) max|v|.
-    The V rows are scaled per block so that r really varies (down to about 1/6).
+    |P8 - P~| <= 2^-4 P~ + 2^-10 / 448 per weight, so each O element moves by
+    at most (2^-4 + 2^-10 / 448 * n_keys / l) * max|v| (ratios with l >= 1).
+    The V rows are scaled per block so that the V block scales differ.
     """
     rng = np.random.default_rng(35)
     x = {n: rng.standard_normal((1, 1, 192, 16)) for n in "qkv"}
@@ -134,11 +133,8 @@ def test_fp8_emulation_p_rounding_within_bound():
     args = (qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1], qc["v"][0], qc["v"][1], 0.25, False)
     o8, l8 = F.fp8_attention_tiled(*args, B_c=64, quantize_p=True)
     o, l = F.fp8_attention_tiled(*args, B_c=64, quantize_p=False)
-    sv = qc["v"][1][0, 0].astype(np.float64)
-    r_min = min(sv[j] / sv[: j + 1].max() for j in range(3))
-    assert r_min < 0.2
     vmax = np.abs(F.dequantize(qc["v"][0], qc["v"][1], 64)).max()
-    bound = (2.0 ** -4 + 2.0 ** -10 / (448 * r_min) * 192) * vmax
+    bound = (2.0 ** -4 + 2.0 ** -10 / 448 * 192) * vmax
     assert np.max(np.abs(o8 - o)) <= bound
     assert np.max(np.abs(o8 - o)) > 0          # the rounding is really applied
     assert np.array_equal(l8, l)                # l comes from the unrounded P~
@@ -147,8 +143,8 @@ def test_fp8_emulation_p_rounding_within_bound():
 def test_fp8_emulation_v_scale_power_of_two_invariance():
     """Multiplying every V block scale by 2^k (same codes) multiplies O by 2^k exactly.
 
-    The ratios r_j = sV_j / max sV are unchanged, so every e4m3 code of P is
-    the same and only the dequantised V is scaled.
+    P and its e4m3 codes do not depend on V, so only the dequantised V is
+    scaled, and by a power of two that rounds nothing.
     """
     rng = np.random.default_rng(36)
     x = {n: rng.standard_normal((1, 2, 150, 8)) for n in "qkv"}
