@@ -69,7 +69,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 constexpr int kQRows = 64;      // rows per scale block
 constexpr int kQThreads = 256;
 constexpr int kQWaves = kQThreads / 64;
-constexpr int kQGrid = 512;     // persistent workgroups (two per compute unit)
+constexpr int kQGrid = 1024;    // persistent workgroups (four per CU where the registers allow)
 constexpr float kMinNormal = 1.17549435e-38f;
 
 enum QuantMode { kBlockScale = 0, kAmaxOnly = 1, kGivenScale = 2 };
