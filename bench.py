@@ -9,8 +9,8 @@ N(0, 1) tensors already resident in device memory.
 FLOP convention: forward 4*B*H*N^2*d, backward 2.5x forward (five matrix
 products), halved for the causal mask.
 
-Prints one JSON line. ``--gpus N`` with N > 1 is refused: this build runs on
-one GPU.
+Prints one JSON line. ``--gpus N`` with N > 1 is refused: the library runs
+the whole workload on one GPU.
 """
 
 from __future__ import annotations
@@ -159,7 +159,7 @@ def main():
                          "size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the attention of each (batch, head) is independent, so heads would shard across GPUs)",
               file=sys.stderr)
         sys.exit(2)

@@ -129,7 +129,8 @@ FA_API int fa_bwd_f32(const float* q, const float* k, const float* v, const floa
  * x8 = e4m3fn(x / s) with x / s a correctly rounded float32 division,
  * rounded to nearest even after saturating to +-448 (x8: [B,H,N,d] bytes,
  * written). Inputs are expected finite: a NaN element gets a NaN code
- * (0x7F or 0xFF) and is left out of its block's amax.
+ * (0x7F or 0xFF) and is left out of its block's amax (with rot, every
+ * element of its row is NaN after the product and is treated so).
  * block_rows = 0 runs three launches and uses scales as scratch between
  * them (every entry ends up holding the one scale). */
 FA_API int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, float* scales,

@@ -82,6 +82,43 @@ def test_quant_exact(fa, block_rows, d, N):
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}"
 
 
+@pytest.mark.parametrize("rotate", [False, True])
+def test_quant_nan_element(fa, rotate):
+    """A NaN element gets a NaN code and is left out of its block's amax.
+
+    With the rotation the NaN reaches every element of its row (x * rot), so
+    the whole row is NaN-coded and the rest of the block sets the scale.
+    """
+    B, H, N, d = 1, 2, 130, 128
+    rng = np.random.default_rng(977)
+    x = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    x[0, 1, 70, 5] = np.nan
+    xt, xv = _bf16_dev(x)
+    rot = si.haar_orthogonal(rng, d).astype(np.float32) if rotate else None
+    import torch
+    announce(f"fa_quant_fp8 NaN element rotate={rotate}")
+    x8, sc = fa.quant_fp8(xt, rot=_to_dev(rot, torch.float32) if rotate else None, block_rows=64)
+    _sync()
+    got_c, got_s = x8.cpu().numpy(), sc.cpu().numpy()
+    clean = xv.copy()
+    clean[0, 1, 70, 5] = 0.0
+    if rotate:
+        nan_c = got_c[0, 1, 70]
+        assert np.all((nan_c & 0x7F) == 0x7F), "row with the NaN is not NaN-coded"
+        rest = np.delete(got_c[0, 1], 70, axis=0)
+        assert not np.any((rest & 0x7F) == 0x7F), "NaN codes outside the NaN row"
+        y = clean.astype(np.float64) @ rot.astype(np.float64)
+        amax = np.abs(np.delete(y[0, 1, 64:128], 70 - 64, axis=0)).max()
+        assert abs(got_s[0, 1, 1] - amax / 448) <= 1e-5 * amax / 448
+    else:
+        assert (got_c[0, 1, 70, 5] & 0x7F) == 0x7F, "NaN element not NaN-coded"
+        codes_ref, s_ref, _ = F.quantize(clean, 64)
+        assert np.array_equal(got_s.view(np.uint32), s_ref.view(np.uint32)), "scales differ"
+        mask = np.ones_like(got_c, dtype=bool)
+        mask[0, 1, 70, 5] = False
+        assert np.array_equal(got_c[mask], codes_ref[mask])
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [17, 200, 1000])
 def test_quant_rotated(fa, d, N):
