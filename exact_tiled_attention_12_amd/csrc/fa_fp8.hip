@@ -27,6 +27,7 @@
 //   * the V block scale differs per tile, so the accumulator is kept in units
 //     of the current tile's scale: before tile j's product it is multiplied by
 //     alpha_j * sV_{j-1} / sV_j, and O = acc * sV_last / l at the end.
+#include <cfloat>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -513,7 +514,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     // Tile scales (a drain step past the last tile keeps the V unit; its
     // exponentials are all zero, whatever c_j is). c_j > 0, so the scaled
     // maximum is c_j times the raw one.
-    const float cj = cq * skj;
+    // c_j > 0 keeps masked scores at -inf after scaling (scale 0 or an
+    // underflowing product would turn -inf * 0 into NaN).
+    const float cj = fmaxf(cq * skj, FLT_MIN);
     const float svj = j < kv_end ? svj_in : sv_cur;
     const float m_new = fmaxf(m, mxr * cj);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;

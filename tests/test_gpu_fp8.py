@@ -207,6 +207,23 @@ def test_fwd_fp8_against_emulation(fa, causal, N):
     assert worst[0] <= 1.0 and worst[1] <= 1.0, worst
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_zero_scale(fa, causal):
+    """scale = 0: every visible key gets the same weight; masked keys none (no NaN from -inf * 0)."""
+    N = 200
+    w = si.Workload(990, "fp8 zero scale", 1, 2, N, 128, "bf16", causal, False)
+    x = si.make_inputs(w, names=("q", "k", "v"))
+    codes = _fp8_codes(x, None)
+    announce(f"fa_fwd_fp8 scale=0 causal={causal}")
+    o, lse = _run_fwd_fp8(fa, codes, 0.0, causal)
+    worst = (0.0, 0.0, 0.0, 0.0)
+    for h in range(w.H):
+        r = _check_rows(o, lse, codes, 0, h, np.arange(N), 0.0, causal)
+        worst = tuple(max(a, b) for a, b in zip(worst, r))
+    print(f"fp8 scale 0 causal={causal}: O err/bound {worst[0]:.3f}, LSE err/bound {worst[1]:.3f}")
+    assert worst[0] <= 1.0 and worst[1] <= 1.0, worst
+
+
 @pytest.fixture(scope="module")
 def workload5(fa):
     """GPU outputs of the fp8 workload, both quantisation schemes, plus the inputs."""
