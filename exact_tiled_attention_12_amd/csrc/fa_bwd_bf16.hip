@@ -278,7 +278,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
         __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + 32));
       lds_barrier();
     }
-    issue_qtile(i + 2);   // into the stage of visit i-1, free after the barrier
 
     const int q0 = qt * kBR;
     const unsigned char* qs = ring(i % kStages);
@@ -322,6 +321,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     };
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // Copies of visit i+2 go to the stage of visit i-1 (free since the
+      // barrier). Issued here rather than right after the barrier, where
+      // they would queue behind the previous visit's dQ atomics and stall.
+      if (kb == 1) issue_qtile(i + 2);
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
       rd_sdp(kb, 0);
