@@ -246,15 +246,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // dQ atomics of the slice (rows of tile qt). A tile that does not exist (or
   // rows past N) gets offsets past the buffer: the atomics are no-ops, so the
   // number of memory operations per tile is the same everywhere.
+  auto dq_atomic = [&](const f32x16& acc, int qt, bool live, int r) INL {
+    const int q = qt * kBR + 8 * (r >> 2) + 4 * hh + (r & 3);
+    const unsigned off = live && q < N ? ((unsigned)q * D + db_q * 32 + l32) * 4 : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rdq, off, 0, 0);
+  };
   auto dq_atomics = [&](const f32x16& acc, int qt, bool live) INL {
-    const int q0 = qt * kBR;
-    const int d = db_q * 32 + l32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const unsigned off = live && q < N ? ((unsigned)q * D + d) * 4 : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rdq, off, 0, 0);
-    }
+    for (int r = 0; r < 16; ++r) dq_atomic(acc, qt, live, r);
   };
 
   __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS));   // K tile, V operands, query tile 0
@@ -390,22 +389,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     Tr4 qop[2];
     qop[0] = rd_dq(sb_prev, 0);
     f32x16 dq_acc = f32x16{};
-    constexpr int QPS = C::NQ / NS;   // dQ products per step
+    // dQ products in the first half of the steps, its atomics spread over
+    // the second half (one burst of 16 would stall on vector-memory issue).
+    constexpr int QPS = 2 * C::NQ / NS;   // dQ products per step, first half
+    constexpr int APS = 2 * 16 / NS;      // dQ atomics per step, second half
 #pragma unroll
     for (int step = 0; step < NS; ++step) {
       const int b = step % 2;
       if (step + 1 < NS) top[(step + 1) % 2] = trd(step + 1);
       __builtin_amdgcn_sched_barrier(0);
       dvdk(1, top[b], step);
+      if (step < NS / 2) {
 #pragma unroll
-      for (int t = 0; t < QPS; ++t) {
-        const int m = step * QPS + t;
-        if (m + 1 < C::NQ) qop[(m + 1) % 2] = rd_dq(sb_prev, m + 1);
-        dq_acc = mma(join(qop[m % 2].v[0], qop[m % 2].v[1]), join(qop[m % 2].v[2], qop[m % 2].v[3]), dq_acc);
+        for (int t = 0; t < QPS; ++t) {
+          const int m = step * QPS + t;
+          if (m + 1 < C::NQ) qop[(m + 1) % 2] = rd_dq(sb_prev, m + 1);
+          dq_acc = mma(join(qop[m % 2].v[0], qop[m % 2].v[1]), join(qop[m % 2].v[2], qop[m % 2].v[3]), dq_acc);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < APS; ++t) dq_atomic(dq_acc, qt + 1, i > 0, (step - NS / 2) * APS + t);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    dq_atomics(dq_acc, qt + 1, i > 0);
   }
 
   // dQ of the last visited tile.
