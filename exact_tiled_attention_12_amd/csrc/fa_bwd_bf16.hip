@@ -389,17 +389,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     Tr4 qop[2];
     qop[0] = rd_dq(sb_prev, 0);
     f32x16 dq_acc = f32x16{};
-    // dQ products in the first half of the steps, its atomics spread over
-    // the second half (one burst of 16 would stall on vector-memory issue).
-    constexpr int QPS = 2 * C::NQ / NS;   // dQ products per step, first half
-    constexpr int APS = 2 * 16 / NS;      // dQ atomics per step, second half
+    // dQ products in the first quarter of the steps, its atomics spread over
+    // the rest (one burst of 16 would stall on vector-memory issue).
+    constexpr int QS = NS / 4;                 // steps that carry dQ products
+    constexpr int QPS = C::NQ / QS;            // dQ products per such step
 #pragma unroll
     for (int step = 0; step < NS; ++step) {
       const int b = step % 2;
       if (step + 1 < NS) top[(step + 1) % 2] = trd(step + 1);
       __builtin_amdgcn_sched_barrier(0);
       dvdk(1, top[b], step);
-      if (step < NS / 2) {
+      if (step < QS) {
 #pragma unroll
         for (int t = 0; t < QPS; ++t) {
           const int m = step * QPS + t;
@@ -407,8 +407,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
           dq_acc = mma(join(qop[m % 2].v[0], qop[m % 2].v[1]), join(qop[m % 2].v[2], qop[m % 2].v[3]), dq_acc);
         }
       } else {
+        // atomics r in [lo, hi) of the 16, split evenly over steps QS .. NS-1
+        constexpr int NA = NS - QS;
+        const int lo = (step - QS) * 16 / NA, hi = (step - QS + 1) * 16 / NA;
 #pragma unroll
-        for (int t = 0; t < APS; ++t) dq_atomic(dq_acc, qt + 1, i > 0, (step - NS / 2) * APS + t);
+        for (int r = lo; r < hi; ++r) dq_atomic(dq_acc, qt + 1, i > 0, r);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
