@@ -571,17 +571,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     l += (part[0] + part[1]) + (part[2] + part[3]);
   };
 
-  // Ring bookkeeping before step j (j >= 1): step j reads K of tiles j+1 and
-  // j+2 and V of tiles j-1 and j, so tile j+2 must be resident while tiles
-  // j+3 .. j+5 stay in flight; tile j-2 was last read by step j-1, so its
-  // stage takes tile j+6.
-  auto tile_sync = [&](int j, auto nst) INL {
-    __builtin_amdgcn_s_waitcnt(wait_vm(6));
+  // Ring bookkeeping, once every two steps, before step j (j even, j >= 2):
+  // steps j and j+1 read K of tiles j+1 .. j+3 and V of tiles j-1 .. j+1, so
+  // tile j+3 must be resident while tile j+4 stays in flight; tiles j-3 and
+  // j-2 were last read by step j-1, so their stages take tiles j+5 and j+6.
+  auto pair_sync = [&](int j, auto st5, auto st6) INL {
+    __builtin_amdgcn_s_waitcnt(wait_vm(2));
     ring_barrier();
-    issue_tile(j + 6, nst);
+    issue_tile(j + 5, st5);
+    issue_tile(j + 6, st6);
   };
 
-  // Prologue: tiles 0..6 in flight, tiles 0..2 resident; S of tile 0;
+  // Prologue: tiles 0..6 in flight, tiles 0..3 resident; S of tile 0;
   // step 0 (its product with V is of a zero P against tile 0's V, which is
   // finite).
   issue_tile(0, IC<0>{});
@@ -591,7 +592,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   issue_tile(4, IC<4>{});
   issue_tile(5, IC<5>{});
   issue_tile(6, IC<6>{});
-  __builtin_amdgcn_s_waitcnt(wait_vm(8));
+  __builtin_amdgcn_s_waitcnt(wait_vm(6));
   ring_barrier();
 
   f32x16 sa[2], sb[2];
@@ -639,7 +640,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   auto one = [&](auto s_tag, int j0) INL -> bool {
     constexpr int S = decltype(s_tag)::value;   // j = j0 + S, j0 = 1 (mod 8)
     const int j = j0 + S;
-    tile_sync(j, IC<(S + 7) % kStages>{});
+    if constexpr (S % 2 == 1) pair_sync(j, IC<(S + 6) % kStages>{}, IC<(S + 7) % kStages>{});
     const unsigned char* kt = ktile(IC<(S + 2) % kStages>{});
     const unsigned char* vt = vtile(IC<S % kStages>{});
     const unsigned char* nkt = ktile(IC<(S + 3) % kStages>{});
