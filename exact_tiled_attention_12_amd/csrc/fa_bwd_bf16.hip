@@ -298,9 +298,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     // P (dP - D). Entry (q0 + ql, key) is kept iff ql >= lim.
     f32x16 s[2], dp[2];
     bf16x8 pf[2][2], df[2][2];
-    auto soft = [&](int kb, int r) INL {
+    constexpr int SPK = 16 / C::KSTEPS;   // softmax evaluations per d step (= per dV/dK step)
+    static_assert(SPK == 16 / (2 * C::DBLK), "one evaluation count per step");
+    // L (times log2 e) and D of the row slots r0 .. r0+SPK-1, read from LDS one
+    // step before their use, ahead of that step's operand reads: waiting for
+    // them then never waits for the operands of the step after.
+    struct LDv {
+      float l[SPK], d[SPK];
+    };
+    auto rd_ld = [&](int r0) INL {
+      LDv v;
+#pragma unroll
+      for (int t = 0; t < SPK; ++t) {
+        const int ql = slot_key(r0 + t, hh);
+        v.l[t] = *LDS(const float, Ls + ql);
+        v.d[t] = *LDS(const float, Ds + ql);
+      }
+      return v;
+    };
+    auto soft = [&](int kb, int r, const LDv& ld) INL {
       const int ql = slot_key(r, hh);
-      const float l2 = *LDS(const float, Ls + ql) * kLog2e, dd = *LDS(const float, Ds + ql);
+      const float l2 = ld.l[r % SPK] * kLog2e, dd = ld.d[r % SPK];
       float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -l2));
       p = ql >= lim[kb] ? p : 0.f;
       const float ds = p * (dp[kb][r] - dd);
@@ -312,6 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     // beside the softmax of block 0 (two evaluations per d step); operands
     // read one step ahead.
     bf16x8 fq[2], fg[2], fk[2];
+    LDv ldv[2];
     auto rd_sdp = [&](int kb, int kk) INL {
       const int b = kk % 2;
       fq[b] = *LDS(bf16x8, qs + (a_lane ^ (32u * kk)));
@@ -326,18 +345,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       if (kb == 1) issue_qtile(i + 2);
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
+      if (kb == 1) ldv[0] = rd_ld(0);
       rd_sdp(kb, 0);
-      constexpr int SPK = 16 / C::KSTEPS;
 #pragma unroll
       for (int kk = 0; kk < C::KSTEPS; ++kk) {
         const int b = kk % 2;
-        if (kk + 1 < C::KSTEPS) rd_sdp(kb, kk + 1);
+        if (kk + 1 < C::KSTEPS) {
+          if (kb == 1) ldv[(kk + 1) % 2] = rd_ld((kk + 1) * SPK);
+          rd_sdp(kb, kk + 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
         s[kb] = mma(fq[b], fk[b], s[kb]);
         dp[kb] = mma(fg[b], vf[kb][kk], dp[kb]);
         if (kb == 1) {
 #pragma unroll
-          for (int t = 0; t < SPK; ++t) soft(0, kk * SPK + t);
+          for (int t = 0; t < SPK; ++t) soft(0, kk * SPK + t, ldv[b]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -365,16 +387,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       dk[kb][db] = mma(df[kb][ks], join(t.v[2], t.v[3]), dk[kb][db]);
     };
     Tr4 top[2];
+    ldv[0] = rd_ld(0);
     top[0] = trd(0);
-    constexpr int SPS = 16 / NS;      // softmax evaluations per step
+    constexpr int SPS = SPK;          // softmax evaluations per step
 #pragma unroll
     for (int step = 0; step < NS; ++step) {
       const int b = step % 2;
-      if (step + 1 < NS) top[(step + 1) % 2] = trd(step + 1);
+      if (step + 1 < NS) {
+        ldv[(step + 1) % 2] = rd_ld((step + 1) * SPS);
+        top[(step + 1) % 2] = trd(step + 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       dvdk(0, top[b], step);
 #pragma unroll
-      for (int t = 0; t < SPS; ++t) soft(1, step * SPS + t);
+      for (int t = 0; t < SPS; ++t) soft(1, step * SPS + t, ldv[b]);
       __builtin_amdgcn_sched_barrier(0);
     }
     {
