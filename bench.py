@@ -143,6 +143,38 @@ def fp8_section(fa, steps: int, warmup: int):
             "fwd_frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
 
 
+def det_section(fa, q, k, v, o, lse, do, causal: bool, steps: int, warmup: int, bwd_ms: float):
+    """Times the fixed-order (deterministic) backward, fa_bwd_det, on the same
+    tensors as the main step: all three launches of one call per step."""
+    import numpy as np
+    import torch
+    B, H, N, d = q.shape
+    ws = torch.empty(fa.bwd_det_workspace_bytes(B, H, N, d, causal), device=q.device, dtype=torch.uint8)
+    out = [torch.empty_like(q) for _ in range(3)]
+
+    def run():
+        fa.bwd(q, k, v, o, lse, do, causal=causal, workspace=ws, dq=out[0], dk=out[1], dv=out[2],
+               deterministic=True)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        run()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    tf = attention_flops(B, H, N, d, causal, True) / (ms * 1e-3) / 1e12
+    res = {"workload": f"fixed-order backward, B={B} H={H} N={N} d={d}, causal={causal}",
+           "bwd_ms": round(ms, 4), "bwd_tflops": round(tf, 2),
+           "workspace_gb": round(ws.numel() / 1e9, 3),
+           "time_vs_atomic_bwd": round(ms / bwd_ms, 4) if bwd_ms > 0 else None}
+    del ws
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +183,7 @@ def main():
     ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 workload timing")
+    ap.add_argument("--no-det", action="store_true", help="skip the fixed-order backward timing")
     ap.add_argument("--fp8-only", action="store_true",
                     help="time only the fp8 workload and print its figures as one JSON line")
     ap.add_argument("--cpu-heads", type=int, default=1)
@@ -270,8 +303,12 @@ def main():
                       "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if do_bwd else None},
         "roofline": roofline,
     }
+    if do_bwd and not args.no_det:
+        del ws
+        torch.cuda.empty_cache()
+        out["bwd_det"] = det_section(fa, q, k, v, o, lse, do, True, args.steps, args.warmup, bwd_ms)
     if not args.no_fp8:
-        del q, k, v, do, o, lse, dq, dk, dv, ws
+        del q, k, v, do, o, lse, dq, dk, dv
         torch.cuda.empty_cache()
         out["fp8"] = fp8_section(fa, args.steps, args.warmup)
     if not args.no_cpu_baseline:

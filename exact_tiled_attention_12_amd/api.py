@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "quant_fp8", "fwd_fp8"]
+__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "bwd_det_workspace_bytes", "quant_fp8", "fwd_fp8"]
 
 
 def _stream(t: torch.Tensor):
@@ -70,11 +70,40 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(_lib.load().fa_bwd_workspace_bytes(B, H, N, d))
 
 
+def bwd_det_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    return int(_lib.load().fa_bwd_det_workspace_bytes(B, H, N, d, int(bool(causal))))
+
+
 def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
-        workspace=None, dq=None, dk=None, dv=None):
-    """dQ, dK, dV of sum(O * dO), recomputing P from LSE. bf16 or float32."""
+        workspace=None, dq=None, dk=None, dv=None, deterministic: bool = False):
+    """dQ, dK, dV of sum(O * dO), recomputing P from LSE. bf16 or float32.
+
+    deterministic=True (bf16 only) calls fa_bwd_det: dQ is reduced over key
+    tiles in a fixed order, so every output is bit-identical from run to run.
+    """
     B, H, N, d = _shape4(q)
     dt = q.dtype
+    if deterministic:
+        if dt != torch.bfloat16:
+            raise ValueError("the fixed-order backward takes bf16 tensors")
+        for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+            _check_tensor(t, n, dt, (B, H, N, d))
+        _check_tensor(lse, "lse", torch.float32, (B, H, N))
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        if workspace is None:
+            workspace = torch.empty(bwd_det_workspace_bytes(B, H, N, d, causal), device=q.device, dtype=torch.uint8)
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(q) if dk is None else dk
+        dv = torch.empty_like(q) if dv is None else dv
+        for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+            _check_tensor(t, n, dt, (B, H, N, d))
+        st = _lib.load().fa_bwd_det(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    B, H, N, d, float(scale), int(bool(causal)), _stream(q))
+        _lib.check(st, "fa_bwd_det")
+        return dq, dk, dv
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _check_tensor(t, n, dt, (B, H, N, d))
     _check_tensor(lse, "lse", torch.float32, (B, H, N))

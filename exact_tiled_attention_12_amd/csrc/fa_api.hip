@@ -100,15 +100,18 @@ int fwd_common(fa::DType dt, const void* q, const void* k, const void* v, void* 
 
 int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, int B, int H, int N,
-               int d, float scale, int causal, void* stream, int stage_mask = 7) {
+               int d, float scale, int causal, void* stream, int stage_mask = 7, bool det = false) {
   if (stage_mask < 1 || stage_mask > 7) return fail(FA_ERR_INVALID, "stage_mask must be in 1..7 (got %d)", stage_mask);
   int rc = check_shape(B, H, N, d, scale);
   if (rc) return rc;
-  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  if (det && (size_t)fa::bwd_row_tiles(N) * fa::kBwdPartFloats * 4 > (1u << 31))
+    return fail(FA_ERR_UNSUPPORTED, "sequence too long for the fixed-order backward (N = %d)", N);
+  const size_t need = det ? fa_bwd_det_workspace_bytes(B, H, N, d, causal) : fa_bwd_workspace_bytes(B, H, N, d);
   if (ws == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
   if ((uintptr_t)ws % 256 != 0) return fail(FA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   if (ws_bytes < need)
-    return fail(FA_ERR_INVALID, "workspace has %zu bytes, needs fa_bwd_workspace_bytes() = %zu", ws_bytes, need);
+    return fail(FA_ERR_INVALID, "workspace has %zu bytes, needs %s() = %zu", ws_bytes,
+                det ? "fa_bwd_det_workspace_bytes" : "fa_bwd_workspace_bytes", need);
   const size_t e = dt == fa::DType::BF16 ? 2 : 4;
   const size_t tb = (size_t)B * H * N * d * e, lb = (size_t)B * H * N * 4;
   const Buf in[6] = {{q, tb, "q", 16},   {k, tb, "k", 16},     {v, tb, "v", 16},
@@ -116,9 +119,18 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   const Buf out[4] = {{dq, tb, "dq", 16}, {dk, tb, "dk", 16}, {dv, tb, "dv", 16}, {ws, need, "workspace", 256}};
   rc = check_bufs(in, 6, out, 4);
   if (rc) return rc;
-  const size_t acc_bytes = align256((size_t)B * H * N * d * 4);
-  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)ws, (float*)((char*)ws + acc_bytes),
-                N, 0, scale, log2e_scale(scale), 0};
+  fa::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.N = N; a.scale = scale; a.c = log2e_scale(scale);
+  if (det) {
+    // D first, then the partial tiles.
+    a.dvec = (float*)ws;
+    a.dq_part = (float*)((char*)ws + align256((size_t)B * H * N * 4));
+  } else {
+    a.dq_acc = (float*)ws;
+    a.dvec = (float*)((char*)ws + align256((size_t)B * H * N * d * 4));
+  }
   return launched(fa::launch_bwd(dt, d, causal, a, B, H, stage_mask, (hipStream_t)stream), "attention backward");
 }
 
@@ -165,6 +177,21 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
                   float scale, int causal, int stage_mask, void* stream) {
   return bwd_common(fa::DType::BF16, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                     scale, causal, stream, stage_mask);
+}
+
+size_t fa_bwd_det_workspace_bytes(int B, int H, int N, int d, int causal) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  const size_t parts = (size_t)fa::bwd_det_parts(N, causal ? 1 : 0);
+  const size_t bh = (size_t)B * H;
+  if (parts > SIZE_MAX / 4 / fa::kBwdPartFloats / bh) return 0;
+  return align256(bh * N * 4) + align256(bh * parts * fa::kBwdPartFloats * 4);
+}
+
+int fa_bwd_det(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+  return bwd_common(fa::DType::BF16, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                    scale, causal, stream, 7, true);
 }
 
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,

@@ -47,6 +47,7 @@ constexpr int kKW = 64;              // keys per wave
 constexpr int kBC = kKW * kWaves;    // keys per workgroup
 constexpr int kBR = 32;              // query rows per tile
 constexpr int kStages = 3;           // query-tile ring depth
+static_assert(kBC == kBwdKeyTile && kBR == kBwdRowTile, "partial-tile layout of the fixed-order dQ");
 
 #define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -109,7 +110,9 @@ __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 #define INL __attribute__((always_inline)) __device__
 
-template <int D, bool CAUSAL>
+// DET: dQ contributions go to partial tiles (plain stores, one tile per
+// visited (key tile, query tile) pair) instead of float32 atomics.
+template <int D, bool CAUSAL, bool DET>
 __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // Device pass only (the host pass needs just the launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -140,10 +143,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   const i32x4 rl = dma_rsrc(a.lse + (size_t)bh * N, (unsigned)N * 4);
   const i32x4 rd = dma_rsrc(a.dvec + (size_t)bh * N, (unsigned)N * 4);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(a.dq_acc + base, (unsigned)N * D * 4);
 
   const int k0 = kt * kBC;
   const int kw0 = k0 + wave * kKW;
+  // dQ destination, addressed by query row: the float32 accumulator of the
+  // head, or (DET) this key tile's partial rows. Those hold rows from the
+  // first visited query tile on (and, for d = 64, one block of them per key
+  // half), so the base is moved back by the rows before that tile.
+  const int n_qt = (N + kBR - 1) / kBR;
+  const int qt_begin = CAUSAL ? k0 / kBR : 0;
+  const int nt = n_qt - qt_begin;   // query tiles this workgroup visits (>= 1)
+  const __amdgpu_buffer_rsrc_t rdq =
+      DET ? make_rsrc(a.dq_part + ((size_t)bh * (size_t)bwd_det_parts(N, CAUSAL) +
+                                   (size_t)bwd_part_offset(N, CAUSAL, kt)) * kBwdPartFloats +
+                          (size_t)(D == 64 ? (wave >> 1) : 0) * nt * kBR * D - (size_t)qt_begin * kBR * D,
+                      (unsigned)n_qt * kBR * D * 4)
+          : make_rsrc(a.dq_acc + base, (unsigned)N * D * 4);
   const unsigned kt_a = (unsigned)(uintptr_t)LDS(unsigned char, kt_s);
   const unsigned rg_a = (unsigned)(uintptr_t)LDS(unsigned char, rg_s);
 
@@ -154,9 +169,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     const unsigned g = live ? (unsigned)(row0 + row) * C::RB + 16 * (p ^ swz<D>(row)) : 0x80000000u;
     dma_load16(r, dst + t * 1024, g);
   };
-  const int n_qt = (N + kBR - 1) / kBR;
-  const int qt_begin = CAUSAL ? k0 / kBR : 0;
-  const int nt = n_qt - qt_begin;   // query tiles this workgroup visits (>= 1)
   // Every wave issues R_LOADS copies per tile: its share of Q and dO, and one
   // copy of L (even waves) or D (odd waves) of the tile's 32 rows; lanes 8..63
   // of that copy read past the row range and write zeros behind it. Two
@@ -243,17 +255,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     t.v[3] = tr_read(kt_s + (t_lane[1] ^ (64u * db_q)) + kc * 16 * C::RB);
     return t;
   };
-  // dQ atomics of the slice (rows of tile qt). A tile that does not exist (or
-  // rows past N) gets offsets past the buffer: the atomics are no-ops, so the
-  // number of memory operations per tile is the same everywhere.
-  auto dq_atomic = [&](const f32x16& acc, int qt, bool live, int r) INL {
-    const int q = qt * kBR + 8 * (r >> 2) + 4 * hh + (r & 3);
+  // dQ atomics (DET: stores) of the slice, rows of the query tile of visit
+  // `visit`, at the rows' own offsets in rdq. A tile that does not exist (or
+  // rows past N) gets offsets past the buffer: the operations are no-ops, so
+  // the number of memory operations per tile is the same everywhere.
+  auto dq_atomic = [&](const f32x16& acc, int visit, bool live, int r) INL {
+    const int q = (n_qt - 1 - visit) * kBR + 8 * (r >> 2) + 4 * hh + (r & 3);
     const unsigned off = live && q < N ? ((unsigned)q * D + db_q * 32 + l32) * 4 : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rdq, off, 0, 0);
+    if constexpr (DET) {
+      // (Bit cast of a copy: hipcc compiled a bit cast applied directly to an
+      // element of a vector variable as a cast of its first element.)
+      const float x = acc[r];
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), rdq, off, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rdq, off, 0, 0);
+    }
   };
-  auto dq_atomics = [&](const f32x16& acc, int qt, bool live) INL {
+  constexpr int NDQ = 16;   // dQ memory operations per visit
+  auto dq_atomics = [&](const f32x16& acc, int visit, bool live) INL {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dq_atomic(acc, qt, live, r);
+    for (int r = 0; r < NDQ; ++r) dq_atomic(acc, visit, live, r);
   };
 
   __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS));   // K tile, V operands, query tile 0
@@ -268,13 +289,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   for (int i = 0; i < nt; ++i) {
     const int qt = n_qt - 1 - i;
     if (i > 0) {
-      // Memory operations issued after visit i's own copies: (i >= 2) the 16
-      // dQ atomics of visit i-2, then the copies of visit i+1 and the 16 dQ
-      // atomics of visit i-1.
+      // Memory operations issued after visit i's own copies: (i >= 2) the NDQ
+      // dQ operations of visit i-2, then the copies of visit i+1 and the NDQ
+      // dQ operations of visit i-1.
       if (i == 1)
-        __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + 16));
+        __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + NDQ));
       else
-        __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + 32));
+        __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + 2 * NDQ));
       lds_barrier();
     }
 
@@ -433,11 +454,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
           dq_acc = mma(join(qop[m % 2].v[0], qop[m % 2].v[1]), join(qop[m % 2].v[2], qop[m % 2].v[3]), dq_acc);
         }
       } else {
-        // atomics r in [lo, hi) of the 16, split evenly over steps QS .. NS-1
+        // memory operations r in [lo, hi) of the NDQ, split evenly over steps QS .. NS-1
         constexpr int NA = NS - QS;
-        const int lo = (step - QS) * 16 / NA, hi = (step - QS + 1) * 16 / NA;
+        const int lo = (step - QS) * NDQ / NA, hi = (step - QS + 1) * NDQ / NA;
 #pragma unroll
-        for (int r = lo; r < hi; ++r) dq_atomic(dq_acc, qt + 1, i > 0, r);
+        for (int r = lo; r < hi; ++r) dq_atomic(dq_acc, i - 1, i > 0, r);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -458,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       dq_acc = mma(join(qop[m % 3].v[0], qop[m % 3].v[1]), join(qop[m % 3].v[2], qop[m % 3].v[3]), dq_acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    dq_atomics(dq_acc, qt_begin, true);
+    dq_atomics(dq_acc, nt - 1, true);
   }
 
   // Epilogue: dK = scale * acc, dV = acc (lanes = d, rows = keys); rows past N dropped.
@@ -484,18 +505,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 #endif
 }
 
+template <int D, bool CAUSAL, bool DET>
+void launch_main(const BwdArgs& a, long long grid, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, DET>), dim3(grid), dim3(kThreads), 0, s, a);
+}
+
 }  // namespace
 
 hipError_t launch_bwd_bf16_main(int d, int causal, BwdArgs a, int B, int H, hipStream_t s) {
   a.n_tiles = (a.N + kBC - 1) / kBC;
   const long long grid = (long long)B * H * a.n_tiles;
   a.remap = grid % 8 == 0 ? 1 : 0;
+  const bool det = a.dq_part != nullptr;
   if (d == 64) {
-    if (causal) hipLaunchKernelGGL((bwd_bf16_kernel<64, true>), dim3(grid), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((bwd_bf16_kernel<64, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    if (causal) det ? launch_main<64, true, true>(a, grid, s) : launch_main<64, true, false>(a, grid, s);
+    else det ? launch_main<64, false, true>(a, grid, s) : launch_main<64, false, false>(a, grid, s);
   } else {
-    if (causal) hipLaunchKernelGGL((bwd_bf16_kernel<128, true>), dim3(grid), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((bwd_bf16_kernel<128, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    if (causal) det ? launch_main<128, true, true>(a, grid, s) : launch_main<128, true, false>(a, grid, s);
+    else det ? launch_main<128, false, true>(a, grid, s) : launch_main<128, false, false>(a, grid, s);
   }
   return hipGetLastError();
 }

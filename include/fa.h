@@ -110,6 +110,28 @@ FA_API int fa_bwd_stages(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes,
                          int B, int H, int N, int d, float scale, int causal, int stage_mask, void* stream);
 
+/* Fixed-order (deterministic) backward, bf16 ("FlashAttention v1～v4 完整进化史",
+ * v4 part 4: a deterministic backward reduces dQ across workgroups in a
+ * fixed order). Same arguments, layouts, checks and mathematics as fa_bwd,
+ * but dq is bit-identical from run to run: every (256-key tile, 32-row
+ * query tile) pair the backward visits writes its float32 dQ contribution
+ * to a partial tile of its own (no atomics), and a final pass adds the
+ * partials of each row in ascending key-tile order, scales and rounds to
+ * bf16 once. dk and dv are bit-identical to fa_bwd's.
+ * workspace: device memory of at least
+ * fa_bwd_det_workspace_bytes(B,H,N,d,causal) bytes, 256-byte aligned;
+ * contents undefined on entry and exit. */
+FA_API int fa_bwd_det(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Bytes of device workspace fa_bwd_det needs: D [B,H,N] float32 plus one
+ * 16 KiB float32 partial tile per visited (256-key tile, 32-row query tile)
+ * pair, i.e. about 2 B H N^2 bytes (causal: about half of that), each part
+ * rounded up to 256 bytes. Returns 0 for invalid sizes. */
+FA_API size_t fa_bwd_det_workspace_bytes(int B, int H, int N, int d, int causal);
+
 /* Backward, float32 tensors. Same contract as fa_bwd. */
 FA_API int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
                const float* dout, float* dq, float* dk, float* dv,

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -128,3 +128,51 @@ def test_fp8_rejects(lib):
                           1, 1, 64, 64, 0.125, 0, None) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_fwd_fp8(A, A + GAP, A + 2 * GAP, s, s + GAP, s + 2 * GAP, A + 256, s + 4 * GAP,
                           1, 1, 64, 128, 0.125, 0, None) == _lib.FA_ERR_INVALID
+
+
+def _det_parts(N, causal):
+    """Visited (256-key tile, 32-row query tile) pairs, counted one by one."""
+    n_qt, n_kt = -(-N // 32), -(-N // 256)
+    return sum(1 for kt in range(n_kt) for qt in range(n_qt) if not causal or qt * 32 >= kt * 256)
+
+
+def test_det_workspace_counts_visited_pairs(lib):
+    def al(x):
+        return (x + 255) // 256 * 256
+    for (B, H, N, d, causal) in [(1, 1, 1, 64, 0), (1, 1, 1, 64, 1), (2, 3, 1000, 128, 1), (2, 3, 1000, 64, 0),
+                                 (1, 2, 257, 128, 1), (1, 32, 16384, 128, 1), (1, 32, 16384, 128, 0)]:
+        got = lib.fa_bwd_det_workspace_bytes(B, H, N, d, causal)
+        assert got == al(4 * B * H * N) + al(B * H * _det_parts(N, causal) * 4096 * 4), (B, H, N, d, causal)
+    # causal keeps only the pairs at or below the diagonal: about half
+    full = lib.fa_bwd_det_workspace_bytes(1, 32, 16384, 128, 0)
+    half = lib.fa_bwd_det_workspace_bytes(1, 32, 16384, 128, 1)
+    assert 0.5 < half / full < 0.52
+    assert lib.fa_bwd_det_workspace_bytes(0, 1, 1, 64, 0) == 0
+    assert lib.fa_bwd_det_workspace_bytes(1, 1, 1, 100, 1) == 0
+
+
+def _bwd_det(lib, ws=A + 10 * GAP, ws_bytes=None, B=1, H=1, N=16, d=64, scale=0.125, causal=1, **over):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_det_workspace_bytes(B, H, N, d, causal)
+    p = dict(q=A, k=A + GAP, v=A + 2 * GAP, o=A + 3 * GAP, lse=A + 4 * GAP, do=A + 5 * GAP,
+             dq=A + 6 * GAP, dk=A + 7 * GAP, dv=A + 8 * GAP)
+    p.update(over)
+    return lib.fa_bwd_det(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                          ws, ws_bytes, B, H, N, d, scale, causal, None)
+
+
+def test_det_backward_rejects(lib):
+    assert _bwd_det(lib, ws=None) == _lib.FA_ERR_INVALID
+    assert _bwd_det(lib, ws=A + 10 * GAP + 16) == _lib.FA_ERR_UNSUPPORTED
+    # the plain backward's (smaller) workspace is not enough
+    N = 1000
+    small = lib.fa_bwd_workspace_bytes(1, 1, N, 64)
+    assert small < lib.fa_bwd_det_workspace_bytes(1, 1, N, 64, 1)
+    assert _bwd_det(lib, N=N, ws_bytes=small) == _lib.FA_ERR_INVALID
+    assert "fa_bwd_det_workspace_bytes" in lib.fa_last_error().decode()
+    # the non-causal layout needs more than the causal one
+    assert _bwd_det(lib, N=N, causal=0, ws_bytes=lib.fa_bwd_det_workspace_bytes(1, 1, N, 64, 1)) == \
+        _lib.FA_ERR_INVALID
+    assert _bwd_det(lib, dq=A + 64) == _lib.FA_ERR_INVALID
+    assert _bwd_det(lib, d=32) == _lib.FA_ERR_UNSUPPORTED
+    assert _bwd_det(lib, scale=float("nan")) == _lib.FA_ERR_UNSUPPORTED
