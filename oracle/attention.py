@@ -40,7 +40,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["scores", "safe_softmax", "forward", "backward", "forward_rows",
-           "backward_head"]
+           "backward_head", "kv_head", "forward_gqa", "backward_gqa"]
 
 
 def _f64(x) -> np.ndarray:
@@ -196,4 +196,56 @@ def backward(q, k, v, do, scale: float, causal: bool = False, row_chunk: int = 1
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = backward_head(
                 q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, row_chunk)
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Grouped-query (GQA) and multi-query (MQA) attention.
+#
+# "FlashAttention v1～v4 完整进化史" names MQA and GQA ("最容易误解的六件事",
+# third item; and the closing list of features to check a backend for) without
+# defining them. Reading: the H query heads are split into H_kv groups of
+# G = H / H_kv consecutive heads, and every head of group j attends with K and
+# V head j (MQA: H_kv = 1; H_kv = H is ordinary multi-head attention). Each
+# query head computes exactly the attention above with its group's K and V; a
+# K or V head read by several query heads receives the sum of their gradients
+# (the chain rule for a shared input).
+
+
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """K/V head read by query head h (groups of H / H_kv consecutive heads)."""
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"H = {H} is not a multiple of H_kv = {H_kv}")
+    return h // (H // H_kv)
+
+
+def forward_gqa(q, k, v, scale: float, causal: bool = False, row_chunk: int = 1024):
+    """(O, LSE) for q [B, H, N, d] with k, v [B, H_kv, N, d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, _ = q.shape
+    H_kv = k.shape[1]
+    o = np.empty(q.shape[:-1] + (v.shape[-1],), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            j = kv_head(h, H, H_kv)
+            o[b, h], lse[b, h] = _head_forward(q[b, h], k[b, j], v[b, j], scale, causal, row_chunk)
+    return o, lse
+
+
+def backward_gqa(q, k, v, do, scale: float, causal: bool = False, row_chunk: int = 1024):
+    """(dQ, dK, dV): dQ per query head; dK, dV [B, H_kv, N, d] summed over the
+    query heads of each group, in ascending head order."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H = q.shape[:2]
+    H_kv = k.shape[1]
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            j = kv_head(h, H, H_kv)
+            dq[b, h], dk_h, dv_h = backward_head(q[b, h], k[b, j], v[b, j], do[b, h], scale, causal, row_chunk)
+            dk[b, j] += dk_h
+            dv[b, j] += dv_h
     return dq, dk, dv
