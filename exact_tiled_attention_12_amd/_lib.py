@@ -29,6 +29,9 @@ SIGNATURES = {
                         _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
     "fa_bwd_stages": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
                                _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _p]),
+    "fa_fwd_gqa": (_c_int, [_p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
+    "fa_bwd_gqa": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
+                            _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
     "fa_bwd_det": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
     "fa_bwd_det_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),

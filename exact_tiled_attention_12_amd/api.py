@@ -42,14 +42,29 @@ def _shape4(q: torch.Tensor):
     return tuple(int(x) for x in q.shape)
 
 
+def _kv_heads(q, k):
+    """K/V heads of k ([B, H_kv, N, d]); H_kv < H selects grouped-query attention (bf16)."""
+    B, H, N, d = _shape4(q)
+    H_kv = int(k.shape[1]) if k.dim() == 4 else -1
+    if H_kv != H and (H_kv < 1 or H % H_kv or q.dtype != torch.bfloat16):
+        raise ValueError(f"k has {H_kv} heads: grouped-query attention needs bf16 and H = {H} a multiple of it")
+    return H_kv
+
+
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """O, LSE = attention(q, k, v). bf16 or float32 inputs; O has the input dtype."""
+    """O, LSE = attention(q, k, v). bf16 or float32 inputs; O has the input dtype.
+
+    k and v may have fewer heads than q (bf16): query head h then attends with
+    K/V head h // (H // H_kv) (grouped-query; one K/V head is multi-query).
+    """
     B, H, N, d = _shape4(q)
     dt = q.dtype
     if dt not in (torch.bfloat16, torch.float32):
         raise TypeError(f"q must be bfloat16 or float32 (got {dt})")
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_tensor(t, n, dt, (B, H, N, d))
+    H_kv = _kv_heads(q, k)
+    _check_tensor(q, "q", dt, (B, H, N, d))
+    for t, n in ((k, "k"), (v, "v")):
+        _check_tensor(t, n, dt, (B, H_kv, N, d))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -59,6 +74,11 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     _check_tensor(out, "out", dt, (B, H, N, d))
     _check_tensor(lse, "lse", torch.float32, (B, H, N))
     lib = _lib.load()
+    if H_kv != H:
+        st = lib.fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, H_kv, N, d, float(scale), int(bool(causal)), _stream(q))
+        _lib.check(st, "fa_fwd_gqa")
+        return out, lse
     fn = lib.fa_fwd if dt == torch.bfloat16 else lib.fa_fwd_f32
     st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             B, H, N, d, float(scale), int(bool(causal)), _stream(q))
@@ -80,9 +100,36 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
 
     deterministic=True (bf16 only) calls fa_bwd_det: dQ is reduced over key
     tiles in a fixed order, so every output is bit-identical from run to run.
+    k and v may have fewer heads than q (bf16, fa_bwd_gqa); dk and dv then
+    have k's shape and sum over each K/V head's query heads.
     """
     B, H, N, d = _shape4(q)
     dt = q.dtype
+    H_kv = _kv_heads(q, k)
+    if H_kv != H:
+        if deterministic:
+            raise ValueError("the fixed-order backward takes one K/V head per query head")
+        for t, n in ((q, "q"), (o, "o"), (do, "do")):
+            _check_tensor(t, n, dt, (B, H, N, d))
+        for t, n in ((k, "k"), (v, "v")):
+            _check_tensor(t, n, dt, (B, H_kv, N, d))
+        _check_tensor(lse, "lse", torch.float32, (B, H, N))
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        if workspace is None:
+            workspace = torch.empty(bwd_workspace_bytes(B, H, N, d), device=q.device, dtype=torch.uint8)
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        _check_tensor(dq, "dq", dt, (B, H, N, d))
+        for t, n in ((dk, "dk"), (dv, "dv")):
+            _check_tensor(t, n, dt, (B, H_kv, N, d))
+        st = _lib.load().fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    B, H, H_kv, N, d, float(scale), int(bool(causal)), _stream(q))
+        _lib.check(st, "fa_bwd_gqa")
+        return dq, dk, dv
     if deterministic:
         if dt != torch.bfloat16:
             raise ValueError("the fixed-order backward takes bf16 tensors")

@@ -84,26 +84,44 @@ int launched(hipError_t e, const char* what) {
 
 float log2e_scale(float scale) { return (float)((double)scale * 1.4426950408889634); }
 
+// K/V heads: 1 <= H_kv <= H with H a multiple of H_kv.
+int check_kv_heads(int H, int H_kv) {
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0)
+    return fail(FA_ERR_INVALID, "H = %d query heads must be a multiple of H_kv = %d >= 1 K/V heads", H, H_kv);
+  return FA_OK;
+}
+
 int fwd_common(fa::DType dt, const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-               int N, int d, float scale, int causal, void* stream) {
+               int N, int d, float scale, int causal, void* stream, int H_kv = 0) {
+  if (H_kv == 0) H_kv = H;   // (callers without grouped heads)
   int rc = check_shape(B, H, N, d, scale);
   if (rc) return rc;
+  rc = check_kv_heads(H, H_kv);
+  if (rc) return rc;
   const size_t e = dt == fa::DType::BF16 ? 2 : 4;
-  const size_t tb = (size_t)B * H * N * d * e, lb = (size_t)B * H * N * 4;
-  const Buf in[3] = {{q, tb, "q", 16}, {k, tb, "k", 16}, {v, tb, "v", 16}};
+  const size_t tb = (size_t)B * H * N * d * e, kb = (size_t)B * H_kv * N * d * e, lb = (size_t)B * H * N * 4;
+  const Buf in[3] = {{q, tb, "q", 16}, {k, kb, "k", 16}, {v, kb, "v", 16}};
   const Buf out[2] = {{o, tb, "o", 16}, {lse, lb, "lse", 4}};
   rc = check_bufs(in, 3, out, 2);
   if (rc) return rc;
-  fa::FwdArgs a{q, k, v, o, lse, N, 0, log2e_scale(scale), 0};
+  fa::FwdArgs a{q, k, v, o, lse, N, 0, log2e_scale(scale), 0, H, H / H_kv};
   return launched(fa::launch_fwd(dt, d, causal, a, B, H, (hipStream_t)stream), "attention forward");
 }
 
 int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, int B, int H, int N,
-               int d, float scale, int causal, void* stream, int stage_mask = 7, bool det = false) {
+               int d, float scale, int causal, void* stream, int stage_mask = 7, bool det = false, int H_kv = 0) {
+  if (H_kv == 0) H_kv = H;   // (callers without grouped heads)
   if (stage_mask < 1 || stage_mask > 7) return fail(FA_ERR_INVALID, "stage_mask must be in 1..7 (got %d)", stage_mask);
   int rc = check_shape(B, H, N, d, scale);
   if (rc) return rc;
+  rc = check_kv_heads(H, H_kv);
+  if (rc) return rc;
+  // A K/V head's workgroups address the dQ accumulator rows of all its query
+  // heads with 32-bit byte offsets.
+  if ((long long)(H / H_kv) * N * d * 4 >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "group too large: %d query heads x N = %d x d = %d float32 reach 2^31 bytes",
+                H / H_kv, N, d);
   if (det && (size_t)fa::bwd_row_tiles(N) * fa::kBwdPartFloats * 4 > (1u << 31))
     return fail(FA_ERR_UNSUPPORTED, "sequence too long for the fixed-order backward (N = %d)", N);
   const size_t need = det ? fa_bwd_det_workspace_bytes(B, H, N, d, causal) : fa_bwd_workspace_bytes(B, H, N, d);
@@ -113,16 +131,17 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
     return fail(FA_ERR_INVALID, "workspace has %zu bytes, needs %s() = %zu", ws_bytes,
                 det ? "fa_bwd_det_workspace_bytes" : "fa_bwd_workspace_bytes", need);
   const size_t e = dt == fa::DType::BF16 ? 2 : 4;
-  const size_t tb = (size_t)B * H * N * d * e, lb = (size_t)B * H * N * 4;
-  const Buf in[6] = {{q, tb, "q", 16},   {k, tb, "k", 16},     {v, tb, "v", 16},
+  const size_t tb = (size_t)B * H * N * d * e, kb = (size_t)B * H_kv * N * d * e, lb = (size_t)B * H * N * 4;
+  const Buf in[6] = {{q, tb, "q", 16},   {k, kb, "k", 16},     {v, kb, "v", 16},
                      {o, tb, "o", 16},   {lse, lb, "lse", 4},  {dout, tb, "dout", 16}};
-  const Buf out[4] = {{dq, tb, "dq", 16}, {dk, tb, "dk", 16}, {dv, tb, "dv", 16}, {ws, need, "workspace", 256}};
+  const Buf out[4] = {{dq, tb, "dq", 16}, {dk, kb, "dk", 16}, {dv, kb, "dv", 16}, {ws, need, "workspace", 256}};
   rc = check_bufs(in, 6, out, 4);
   if (rc) return rc;
   fa::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.N = N; a.scale = scale; a.c = log2e_scale(scale);
+  a.H = H; a.group = H / H_kv;
   if (det) {
     // D first, then the partial tiles.
     a.dvec = (float*)ws;
@@ -192,6 +211,20 @@ int fa_bwd_det(const void* q, const void* k, const void* v, const void* o, const
                float scale, int causal, void* stream) {
   return bwd_common(fa::DType::BF16, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                     scale, causal, stream, 7, true);
+}
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
+               int d, float scale, int causal, void* stream) {
+  if (H_kv < 1) return check_kv_heads(H, H_kv);
+  return fwd_common(fa::DType::BF16, q, k, v, o, lse, B, H, N, d, scale, causal, stream, H_kv);
+}
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int H_kv,
+               int N, int d, float scale, int causal, void* stream) {
+  if (H_kv < 1) return check_kv_heads(H, H_kv);
+  return bwd_common(fa::DType::BF16, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                    scale, causal, stream, 7, false, H_kv);
 }
 
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,

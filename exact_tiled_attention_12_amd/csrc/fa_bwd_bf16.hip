@@ -112,7 +112,10 @@ __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // DET: dQ contributions go to partial tiles (plain stores, one tile per
 // visited (key tile, query tile) pair) instead of float32 atomics.
-template <int D, bool CAUSAL, bool DET>
+// GQA: the key tile belongs to a K/V head shared by a.group consecutive query
+// heads; the workgroup visits the query tiles of each of them in turn, so
+// dK and dV sum over the group in registers (a.group == 1 without GQA).
+template <int D, bool CAUSAL, bool DET, bool GQA>
 __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // Device pass only (the host pass needs just the launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -132,16 +135,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
   int wg = blockIdx.x;
   if (a.remap) wg = xcd_remap(wg, gridDim.x);
-  const int bh = wg / a.n_tiles;
+  const int bh = wg / a.n_tiles;            // (batch, K/V head)
   const int kt = wg - bh * a.n_tiles;        // key tile; tile 0 (heaviest when causal) first
   const int N = a.N;
+  const int G = GQA ? a.group : 1;           // query heads per K/V head
+  // First query head of the group (the query heads of K/V head j of batch b
+  // are b H + j G .. b H + j G + G - 1).
+  const int qh0 = GQA ? (bh / (a.H / G)) * a.H + (bh % (a.H / G)) * G : bh;
   const size_t base = (size_t)bh * (size_t)N * D;
+  const size_t qbase = (size_t)qh0 * (size_t)N * D;
   const unsigned head_bytes = (unsigned)N * C::RB;
-  const i32x4 rq = dma_rsrc((const __bf16*)a.q + base, head_bytes);
+  // Query-side buffers start at the group's first head; a visit to head g of
+  // the group shifts its offsets by g heads and ends its buffer at head g's
+  // last row, so rows past N still read as zero.
+  const i32x4 rq = dma_rsrc((const __bf16*)a.q + qbase, head_bytes);
   const i32x4 rk = dma_rsrc((const __bf16*)a.k + base, head_bytes);
-  const i32x4 rg = dma_rsrc((const __bf16*)a.dout + base, head_bytes);
-  const i32x4 rl = dma_rsrc(a.lse + (size_t)bh * N, (unsigned)N * 4);
-  const i32x4 rd = dma_rsrc(a.dvec + (size_t)bh * N, (unsigned)N * 4);
+  const i32x4 rg = dma_rsrc((const __bf16*)a.dout + qbase, head_bytes);
+  const i32x4 rl = dma_rsrc(a.lse + (size_t)qh0 * N, (unsigned)N * 4);
+  const i32x4 rd = dma_rsrc(a.dvec + (size_t)qh0 * N, (unsigned)N * 4);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + base, head_bytes);
 
   const int k0 = kt * kBC;
@@ -152,13 +163,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // half), so the base is moved back by the rows before that tile.
   const int n_qt = (N + kBR - 1) / kBR;
   const int qt_begin = CAUSAL ? k0 / kBR : 0;
-  const int nt = n_qt - qt_begin;   // query tiles this workgroup visits (>= 1)
+  const int nt = n_qt - qt_begin;   // query tiles visited per query head (>= 1)
+  const int nvis = G * nt;          // visits: head 0's tiles, then head 1's, ...
+  // Visit i: query head g = i / nt of the group, tile n_qt - 1 - (i % nt).
+  auto vhead = [&](int i) INL { return GQA ? i / nt : 0; };
+  auto vtile = [&](int i) INL { return n_qt - 1 - (GQA ? i - (i / nt) * nt : i); };
   const __amdgpu_buffer_rsrc_t rdq =
       DET ? make_rsrc(a.dq_part + ((size_t)bh * (size_t)bwd_det_parts(N, CAUSAL) +
                                    (size_t)bwd_part_offset(N, CAUSAL, kt)) * kBwdPartFloats +
                           (size_t)(D == 64 ? (wave >> 1) : 0) * nt * kBR * D - (size_t)qt_begin * kBR * D,
                       (unsigned)n_qt * kBR * D * 4)
-          : make_rsrc(a.dq_acc + base, (unsigned)N * D * 4);
+          : make_rsrc(a.dq_acc + qbase, (unsigned)G * N * D * 4);
   const unsigned kt_a = (unsigned)(uintptr_t)LDS(unsigned char, kt_s);
   const unsigned rg_a = (unsigned)(uintptr_t)LDS(unsigned char, rg_s);
 
@@ -174,21 +189,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // of that copy read past the row range and write zeros behind it. Two
   // waves copy the same L or D bytes to the same place.
   auto issue_qtile = [&](int i) INL {
-    const int qt = n_qt - 1 - i;
-    const bool live = i < nt;
+    const bool live = i < nvis;
+    const int hg = live ? vhead(i) : 0;
+    const int qt = live ? vtile(i) : 0;
+    const int r0 = hg * N + qt * kBR;   // first row, counted from the group's first head
+    i32x4 q_r = rq, g_r = rg, l_r = rl, d_r = rd;
+    if constexpr (GQA) {
+      q_r[2] = g_r[2] = (hg + 1) * (int)head_bytes;
+      l_r[2] = d_r[2] = (hg + 1) * N * 4;
+    }
     const unsigned so = rg_a + (i % kStages) * C::STAGE;
 #pragma unroll
     for (int u = 0; u < C::QT_LOADS; ++u) {
       const int t = wave * C::QT_LOADS + u;
-      copy_rows(rq, so, qt * kBR, t, live);
-      copy_rows(rg, so + C::QT, qt * kBR, t, live);
+      copy_rows(q_r, so, r0, t, live);
+      copy_rows(g_r, so + C::QT, r0, t, live);
     }
-    const unsigned lo = (unsigned)(qt * kBR) * 4 + 16 * lane;
+    const unsigned lo = (unsigned)r0 * 4 + 16 * lane;
     const unsigned off = live && lane < 8 ? lo : 0x80000000u;
     if (wave & 1)
-      dma_load16(rd, so + 2 * C::QT + C::LD, off);
+      dma_load16(d_r, so + 2 * C::QT + C::LD, off);
     else
-      dma_load16(rl, so + 2 * C::QT, off);
+      dma_load16(l_r, so + 2 * C::QT, off);
   };
 
   // K tile (whole workgroup), V operands, then the first two query tiles.
@@ -260,8 +282,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // rows past N) gets offsets past the buffer: the operations are no-ops, so
   // the number of memory operations per tile is the same everywhere.
   auto dq_atomic = [&](const f32x16& acc, int visit, bool live, int r) INL {
-    const int q = (n_qt - 1 - visit) * kBR + 8 * (r >> 2) + 4 * hh + (r & 3);
-    const unsigned off = live && q < N ? ((unsigned)q * D + db_q * 32 + l32) * 4 : 0x80000000u;
+    const int q = vtile(visit) * kBR + 8 * (r >> 2) + 4 * hh + (r & 3);
+    const unsigned off = live && q < N ? ((unsigned)(vhead(visit) * N + q) * D + db_q * 32 + l32) * 4 : 0x80000000u;
     if constexpr (DET) {
       // (Bit cast of a copy: hipcc compiled a bit cast applied directly to an
       // element of a vector variable as a cast of its first element.)
@@ -286,8 +308,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // accumulator. Visit i (query tile qt = n_qt - 1 - i) is in ring stage
   // i % 3; its dS^T goes to dS buffer i % 2, which dQ of visit i reads during
   // visit i + 1.
-  for (int i = 0; i < nt; ++i) {
-    const int qt = n_qt - 1 - i;
+  for (int i = 0; i < nvis; ++i) {
+    const int qt = vtile(i);
     if (i > 0) {
       // Memory operations issued after visit i's own copies: (i >= 2) the NDQ
       // dQ operations of visit i-2, then the copies of visit i+1 and the NDQ
@@ -467,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // dQ of the last visited tile.
   lds_barrier();
   {
-    const unsigned char* sb = dsb((nt - 1) & 1);
+    const unsigned char* sb = dsb((nvis - 1) & 1);
     Tr4 qop[3];
     qop[0] = rd_dq(sb, 0);
     qop[1] = rd_dq(sb, 1);
@@ -479,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       dq_acc = mma(join(qop[m % 3].v[0], qop[m % 3].v[1]), join(qop[m % 3].v[2], qop[m % 3].v[3]), dq_acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    dq_atomics(dq_acc, nt - 1, true);
+    dq_atomics(dq_acc, nvis - 1, true);
   }
 
   // Epilogue: dK = scale * acc, dV = acc (lanes = d, rows = keys); rows past N dropped.
@@ -507,14 +529,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
 template <int D, bool CAUSAL, bool DET>
 void launch_main(const BwdArgs& a, long long grid, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, DET>), dim3(grid), dim3(kThreads), 0, s, a);
+  if constexpr (DET)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (a.group > 1)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, false, false>), dim3(grid), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16_main(int d, int causal, BwdArgs a, int B, int H, hipStream_t s) {
   a.n_tiles = (a.N + kBC - 1) / kBC;
-  const long long grid = (long long)B * H * a.n_tiles;
+  // One workgroup per (batch, K/V head, key tile).
+  const long long grid = (long long)B * (H / a.group) * a.n_tiles;
   a.remap = grid % 8 == 0 ? 1 : 0;
   const bool det = a.dq_part != nullptr;
   if (d == 64) {

@@ -145,10 +145,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int qt = CAUSAL ? (a.n_qtiles - 1 - t) : t;
   const int N = a.N;
   const size_t base = (size_t)bh * (size_t)N * D;
+  // K/V head of this query head: groups of `group` consecutive query heads
+  // share one (grouped-query attention; group = 1 is one K/V head per head).
+  const int kvh = a.group == 1 ? bh : (bh / a.H) * (a.H / a.group) + (bh % a.H) / a.group;
+  const size_t kv_base = (size_t)kvh * (size_t)N * D;
   const unsigned head_bytes = (unsigned)N * C::RB;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)a.q + base, head_bytes);
-  const i32x4 rk = dma_rsrc((const __bf16*)a.k + base, head_bytes);
-  const i32x4 rv = dma_rsrc((const __bf16*)a.v + base, head_bytes);
+  const i32x4 rk = dma_rsrc((const __bf16*)a.k + kv_base, head_bytes);
+  const i32x4 rv = dma_rsrc((const __bf16*)a.v + kv_base, head_bytes);
 
   const int q0 = qt * kBR;
   const int wrow0 = q0 + wave * 32;

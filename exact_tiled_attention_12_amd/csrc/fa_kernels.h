@@ -18,6 +18,8 @@ struct FwdArgs {
   int n_qtiles;   // filled by the launcher
   float c;        // scale * log2(e)
   int remap;      // filled by the launcher
+  int H;          // query heads
+  int group;      // query heads per K/V head (1 unless grouped-query, bf16 only)
 };
 
 struct BwdArgs {
@@ -38,6 +40,8 @@ struct BwdArgs {
   float scale;
   float c;        // scale * log2(e)
   int remap;      // filled by the launcher
+  int H;          // query heads
+  int group;      // query heads per K/V head (1 unless grouped-query, bf16 only)
 };
 
 struct QuantArgs {

@@ -110,6 +110,25 @@ FA_API int fa_bwd_stages(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes,
                          int B, int H, int N, int d, float scale, int causal, int stage_mask, void* stream);
 
+/* Grouped-query and multi-query attention, bf16 ("FlashAttention v1～v4
+ * 完整进化史" names GQA and MQA among the attention features a backend may
+ * support). q, o, dq, dout: [B,H,N,d]; k, v, dk, dv: [B,H_kv,N,d] with H a
+ * multiple of H_kv; lse: [B,H,N]. The H query heads form H_kv groups of
+ * G = H / H_kv consecutive heads, and query head h attends with K/V head
+ * h / G (MQA: H_kv = 1; H_kv = H is fa_fwd / fa_bwd). dk and dv of a K/V
+ * head are the sums over the G query heads that read it; they are summed in
+ * the accumulators of one workgroup, so dk and dv stay deterministic. The
+ * backward's workspace is fa_bwd_workspace_bytes(B, H, N, d) (query heads),
+ * and G * N * d * 4 must be below 2^31 bytes. Same conventions, checks and
+ * rounding as fa_fwd / fa_bwd; H_kv out of range or not dividing H gives
+ * FA_ERR_INVALID. */
+FA_API int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int H_kv, int N, int d, float scale, int causal, void* stream);
+FA_API int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int H, int H_kv, int N, int d, float scale, int causal, void* stream);
+
 /* Fixed-order (deterministic) backward, bf16 ("FlashAttention v1～v4 完整进化史",
  * v4 part 4: a deterministic backward reduces dQ across workgroups in a
  * fixed order). Same arguments, layouts, checks and mathematics as fa_bwd,

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -176,3 +176,28 @@ def test_det_backward_rejects(lib):
     assert _bwd_det(lib, dq=A + 64) == _lib.FA_ERR_INVALID
     assert _bwd_det(lib, d=32) == _lib.FA_ERR_UNSUPPORTED
     assert _bwd_det(lib, scale=float("nan")) == _lib.FA_ERR_UNSUPPORTED
+
+
+def test_gqa_rejects(lib):
+    def fwd(H=4, H_kv=2, N=16, d=64, **over):
+        p = dict(q=A, k=A + GAP, v=A + 2 * GAP, o=A + 3 * GAP, lse=A + 4 * GAP)
+        p.update(over)
+        return lib.fa_fwd_gqa(p["q"], p["k"], p["v"], p["o"], p["lse"], 1, H, H_kv, N, d, 0.125, 1, None)
+
+    def bwd(H=4, H_kv=2, N=16, d=64, ws_bytes=None):
+        if ws_bytes is None:
+            ws_bytes = lib.fa_bwd_workspace_bytes(1, H, N, d)
+        return lib.fa_bwd_gqa(A, A + GAP, A + 2 * GAP, A + 3 * GAP, A + 4 * GAP, A + 5 * GAP, A + 6 * GAP,
+                              A + 7 * GAP, A + 8 * GAP, A + 10 * GAP, ws_bytes, 1, H, H_kv, N, d, 0.125, 1, None)
+
+    for H_kv in (0, -1, 3, 5, 8):
+        assert fwd(H_kv=H_kv) == _lib.FA_ERR_INVALID, H_kv
+        assert "H_kv" in lib.fa_last_error().decode()
+        assert bwd(H_kv=H_kv) == _lib.FA_ERR_INVALID, H_kv
+    assert fwd(d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert fwd(o=A + 256) == _lib.FA_ERR_INVALID          # o overlaps q
+    assert fwd(o=A + GAP + 64) == _lib.FA_ERR_INVALID     # o inside k
+    assert bwd(ws_bytes=100) == _lib.FA_ERR_INVALID
+    # a group's dQ rows must fit 32-bit offsets: 64 heads x N = 2^17 x 64 x 4 bytes
+    assert bwd(H=64, H_kv=1, N=1 << 17, d=64) == _lib.FA_ERR_UNSUPPORTED
+    assert "group too large" in lib.fa_last_error().decode()
