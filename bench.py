@@ -175,6 +175,53 @@ def det_section(fa, q, k, v, o, lse, do, causal: bool, steps: int, warmup: int, 
     return res
 
 
+def gqa_section(fa, steps: int, warmup: int, H_kv_list=(8, 1)):
+    """Times grouped-query (and multi-query) forward + backward at the main
+    workload's shape (B=1, H=32 query heads, N=16384, d=128, causal) with
+    H_kv K/V heads. Inputs: seeded N(0, 1) bf16 tensors drawn on the device."""
+    import numpy as np
+    import torch
+    B, H, N, d = 1, 32, 16384, 128
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    mk = lambda h: torch.randn((B, h, N, d), device="cuda", generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    q, do = mk(H), mk(H)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), device="cuda", dtype=torch.uint8)
+    dq = torch.empty_like(q)
+    res = {}
+    for H_kv in H_kv_list:
+        k, v = mk(H_kv), mk(H_kv)
+        dk, dv = torch.empty_like(k), torch.empty_like(v)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+        def run(e=None):
+            if e:
+                e[0].record()
+            fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+            if e:
+                e[1].record()
+            fa.bwd(q, k, v, o, lse, do, causal=True, workspace=ws, dq=dq, dk=dk, dv=dv)
+            if e:
+                e[2].record()
+
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        for e in ev:
+            run(e)
+        torch.cuda.synchronize()
+        f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        ff, fb = attention_flops(B, H, N, d, True), attention_flops(B, H, N, d, True, True)
+        res[f"H_kv={H_kv}"] = {"fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+                               "fwd_tflops": round(ff / (f_ms * 1e-3) / 1e12, 2),
+                               "bwd_tflops": round(fb / (b_ms * 1e-3) / 1e12, 2),
+                               "tflops": round((ff + fb) / ((f_ms + b_ms) * 1e-3) / 1e12, 2)}
+        del k, v, dk, dv
+    return {"workload": f"grouped-query causal bf16 attention, B={B} H={H} N={N} d={d}, fwd + bwd", **res}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +231,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 workload timing")
     ap.add_argument("--no-det", action="store_true", help="skip the fixed-order backward timing")
+    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query timing")
     ap.add_argument("--fp8-only", action="store_true",
                     help="time only the fp8 workload and print its figures as one JSON line")
     ap.add_argument("--cpu-heads", type=int, default=1)
@@ -307,8 +355,12 @@ def main():
         del ws
         torch.cuda.empty_cache()
         out["bwd_det"] = det_section(fa, q, k, v, o, lse, do, True, args.steps, args.warmup, bwd_ms)
-    if not args.no_fp8:
+    if not args.no_fp8 or (do_bwd and not args.no_gqa):
         del q, k, v, do, o, lse, dq, dk, dv
+        torch.cuda.empty_cache()
+    if do_bwd and not args.no_gqa:
+        out["gqa"] = gqa_section(fa, args.steps, args.warmup)
+    if not args.no_fp8:
         torch.cuda.empty_cache()
         out["fp8"] = fp8_section(fa, args.steps, args.warmup)
     if not args.no_cpu_baseline:

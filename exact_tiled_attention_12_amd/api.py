@@ -12,7 +12,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "bwd_det_workspace_bytes", "quant_fp8", "fwd_fp8"]
+__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "bwd_det_workspace_bytes", "bwd_gqa_workspace_bytes",
+           "quant_fp8", "fwd_fp8"]
 
 
 def _stream(t: torch.Tensor):
@@ -90,6 +91,10 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(_lib.load().fa_bwd_workspace_bytes(B, H, N, d))
 
 
+def bwd_gqa_workspace_bytes(B: int, H: int, H_kv: int, N: int, d: int) -> int:
+    return int(_lib.load().fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, d))
+
+
 def bwd_det_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
     return int(_lib.load().fa_bwd_det_workspace_bytes(B, H, N, d, int(bool(causal))))
 
@@ -117,7 +122,7 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
         if scale is None:
             scale = 1.0 / math.sqrt(d)
         if workspace is None:
-            workspace = torch.empty(bwd_workspace_bytes(B, H, N, d), device=q.device, dtype=torch.uint8)
+            workspace = torch.empty(bwd_gqa_workspace_bytes(B, H, H_kv, N, d), device=q.device, dtype=torch.uint8)
         dq = torch.empty_like(q) if dq is None else dq
         dk = torch.empty_like(k) if dk is None else dk
         dv = torch.empty_like(v) if dv is None else dv

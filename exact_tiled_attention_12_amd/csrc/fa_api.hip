@@ -117,19 +117,22 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   if (rc) return rc;
   rc = check_kv_heads(H, H_kv);
   if (rc) return rc;
-  // A K/V head's workgroups address the dQ accumulator rows of all its query
-  // heads with 32-bit byte offsets.
-  if ((long long)(H / H_kv) * N * d * 4 >= (1LL << 31))
+  // A workgroup addresses the dQ accumulator rows of all the query heads it
+  // visits with 32-bit byte offsets.
+  const int chunks = H_kv < H ? fa::bwd_gqa_chunks(B, H, H_kv, N) : 1;
+  if ((long long)(H / H_kv / chunks) * N * d * 4 >= (1LL << 31))
     return fail(FA_ERR_UNSUPPORTED, "group too large: %d query heads x N = %d x d = %d float32 reach 2^31 bytes",
-                H / H_kv, N, d);
+                H / H_kv / chunks, N, d);
   if (det && (size_t)fa::bwd_row_tiles(N) * fa::kBwdPartFloats * 4 > (1u << 31))
     return fail(FA_ERR_UNSUPPORTED, "sequence too long for the fixed-order backward (N = %d)", N);
-  const size_t need = det ? fa_bwd_det_workspace_bytes(B, H, N, d, causal) : fa_bwd_workspace_bytes(B, H, N, d);
+  const size_t need = det ? fa_bwd_det_workspace_bytes(B, H, N, d, causal)
+                     : H_kv < H ? fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, d) : fa_bwd_workspace_bytes(B, H, N, d);
   if (ws == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
   if ((uintptr_t)ws % 256 != 0) return fail(FA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   if (ws_bytes < need)
     return fail(FA_ERR_INVALID, "workspace has %zu bytes, needs %s() = %zu", ws_bytes,
-                det ? "fa_bwd_det_workspace_bytes" : "fa_bwd_workspace_bytes", need);
+                det ? "fa_bwd_det_workspace_bytes" : H_kv < H ? "fa_bwd_gqa_workspace_bytes" : "fa_bwd_workspace_bytes",
+                need);
   const size_t e = dt == fa::DType::BF16 ? 2 : 4;
   const size_t tb = (size_t)B * H * N * d * e, kb = (size_t)B * H_kv * N * d * e, lb = (size_t)B * H * N * 4;
   const Buf in[6] = {{q, tb, "q", 16},   {k, kb, "k", 16},     {v, kb, "v", 16},
@@ -141,7 +144,7 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.N = N; a.scale = scale; a.c = log2e_scale(scale);
-  a.H = H; a.group = H / H_kv;
+  a.H = H; a.group = H / H_kv; a.hchunks = chunks; a.B = B;
   if (det) {
     // D first, then the partial tiles.
     a.dvec = (float*)ws;
@@ -149,6 +152,8 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   } else {
     a.dq_acc = (float*)ws;
     a.dvec = (float*)((char*)ws + align256((size_t)B * H * N * d * 4));
+    // grouped-query with several head chunks: float32 dK, dV per chunk after D
+    if (chunks > 1) a.dkv_part = (float*)((char*)ws + fa_bwd_workspace_bytes(B, H, N, d));
   }
   return launched(fa::launch_bwd(dt, d, causal, a, B, H, stage_mask, (hipStream_t)stream), "attention backward");
 }
@@ -211,6 +216,14 @@ int fa_bwd_det(const void* q, const void* k, const void* v, const void* o, const
                float scale, int causal, void* stream) {
   return bwd_common(fa::DType::BF16, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                     scale, causal, stream, 7, true);
+}
+
+size_t fa_bwd_gqa_workspace_bytes(int B, int H, int H_kv, int N, int d) {
+  const size_t base = fa_bwd_workspace_bytes(B, H, N, d);
+  if (base == 0 || H_kv < 1 || H_kv > H || H % H_kv != 0) return 0;
+  const int chunks = H_kv < H ? fa::bwd_gqa_chunks(B, H, H_kv, N) : 1;
+  if (chunks == 1) return base;
+  return base + align256((size_t)2 * B * H_kv * chunks * N * d * 4);
 }
 
 int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,

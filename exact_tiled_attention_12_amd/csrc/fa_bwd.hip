@@ -166,6 +166,33 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_det_kernel(BwdArgs a, long lo
   *(u32x2*)((__bf16*)a.dq + row * D + c) = w;
 }
 
+// ------------------------------------- grouped-query dK, dV chunk sum
+// dk, dv [B, H_kv, N, d] = sum over the head chunks c = 0, 1, ... (in that
+// order) of the chunks' float32 dK (already scaled) and dV, rounded to bf16.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkv_sum_kernel(BwdArgs a, long long n4) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n4) return;
+  const long long e = 4 * i;                          // element of [B H_kv][N][d]
+  const long long per_head = (long long)a.N * D;
+  const long long bh = e / per_head, in_head = e - bh * per_head;
+  const int C = a.hchunks;
+  const float* pk = a.dkv_part + (size_t)bh * C * per_head + in_head;
+  const float* pv = pk + (size_t)n4 * 4 * C;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < C; ++c) {
+    sk += __builtin_nontemporal_load((const f32x4*)(pk + (size_t)c * per_head));
+    sv += __builtin_nontemporal_load((const f32x4*)(pv + (size_t)c * per_head));
+  }
+  u32x2 w;
+  w[0] = pack_bf16x2(sk[0], sk[1]);
+  w[1] = pack_bf16x2(sk[2], sk[3]);
+  *(u32x2*)((__bf16*)a.dk + e) = w;
+  w[0] = pack_bf16x2(sv[0], sv[1]);
+  w[1] = pack_bf16x2(sv[2], sv[3]);
+  *(u32x2*)((__bf16*)a.dv + e) = w;
+}
+
 // ---------------------------------------------------------------- main
 template <class Tr, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
@@ -439,6 +466,15 @@ hipError_t run(int causal, BwdArgs a, int B, int H, int stage_mask, hipStream_t 
     hipLaunchKernelGGL((bwd_dq_kernel<Tr, D>), dim3(blocks), dim3(kThreads), 0, s, a, n4);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if constexpr (sizeof(typename Tr::T) == 2) {
+      if (a.dkv_part != nullptr) {   // grouped-query with several head chunks
+        const long long m4 = (long long)B * (H / a.group) * a.N * D / 4;
+        const int mb = (int)((m4 + kThreads - 1) / kThreads);
+        hipLaunchKernelGGL((bwd_dkv_sum_kernel<D>), dim3(mb), dim3(kThreads), 0, s, a, m4);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    }
   }
   return hipSuccess;
 }

@@ -135,13 +135,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
   int wg = blockIdx.x;
   if (a.remap) wg = xcd_remap(wg, gridDim.x);
-  const int bh = wg / a.n_tiles;            // (batch, K/V head)
-  const int kt = wg - bh * a.n_tiles;        // key tile; tile 0 (heaviest when causal) first
+  const int bhc = wg / a.n_tiles;           // (batch, K/V head, chunk)
+  const int kt = wg - bhc * a.n_tiles;       // key tile; tile 0 (heaviest when causal) first
   const int N = a.N;
-  const int G = GQA ? a.group : 1;           // query heads per K/V head
-  // First query head of the group (the query heads of K/V head j of batch b
-  // are b H + j G .. b H + j G + G - 1).
-  const int qh0 = GQA ? (bh / (a.H / G)) * a.H + (bh % (a.H / G)) * G : bh;
+  // (batch, K/V head) and the chunk of its query heads. Without GQA a chunk
+  // is one query head (bhc is the query head); a.group > 1 then means grouped
+  // query heads handled one per workgroup.
+  const int bh = GQA ? bhc / a.hchunks : (a.group == 1 ? bhc : bhc / a.group);
+  const int chunk = bhc - bh * (GQA ? a.hchunks : a.group);
+  const int G = GQA ? a.group / a.hchunks : 1;         // query heads this workgroup visits
+  // First query head of the chunk (the query heads of K/V head j of batch b
+  // are b H + j group .. b H + j group + group - 1).
+  const int qh0 = GQA ? (bh / (a.H / a.group)) * a.H + (bh % (a.H / a.group)) * a.group + chunk * G : bhc;
   const size_t base = (size_t)bh * (size_t)N * D;
   const size_t qbase = (size_t)qh0 * (size_t)N * D;
   const unsigned head_bytes = (unsigned)N * C::RB;
@@ -165,9 +170,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   const int qt_begin = CAUSAL ? k0 / kBR : 0;
   const int nt = n_qt - qt_begin;   // query tiles visited per query head (>= 1)
   const int nvis = G * nt;          // visits: head 0's tiles, then head 1's, ...
-  // Visit i: query head g = i / nt of the group, tile n_qt - 1 - (i % nt).
-  auto vhead = [&](int i) INL { return GQA ? i / nt : 0; };
-  auto vtile = [&](int i) INL { return n_qt - 1 - (GQA ? i - (i / nt) * nt : i); };
+  // Visit i: query head g = i / nt of the chunk, tile n_qt - 1 - (i % nt).
+  // (GQA: the loop forms i / nt once per visit and passes the quotients of
+  // visits i - 1 and i + 2 on, so vhead / vtile take it as an argument.)
+  auto vhead = [&](int i, int q) INL { return GQA ? q : 0; };
+  auto vtile = [&](int i, int q) INL { return n_qt - 1 - (GQA ? i - q * nt : i); };
   const __amdgpu_buffer_rsrc_t rdq =
       DET ? make_rsrc(a.dq_part + ((size_t)bh * (size_t)bwd_det_parts(N, CAUSAL) +
                                    (size_t)bwd_part_offset(N, CAUSAL, kt)) * kBwdPartFloats +
@@ -188,15 +195,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // copy of L (even waves) or D (odd waves) of the tile's 32 rows; lanes 8..63
   // of that copy read past the row range and write zeros behind it. Two
   // waves copy the same L or D bytes to the same place.
-  auto issue_qtile = [&](int i) INL {
+  auto issue_qtile = [&](int i, int iq) INL {
     const bool live = i < nvis;
-    const int hg = live ? vhead(i) : 0;
-    const int qt = live ? vtile(i) : 0;
+    const int hg = live ? vhead(i, iq) : 0;
+    const int qt = live ? vtile(i, iq) : 0;
     const int r0 = hg * N + qt * kBR;   // first row, counted from the group's first head
     i32x4 q_r = rq, g_r = rg, l_r = rl, d_r = rd;
     if constexpr (GQA) {
-      q_r[2] = g_r[2] = (hg + 1) * (int)head_bytes;
-      l_r[2] = d_r[2] = (hg + 1) * N * 4;
+      q_r[2] = g_r[2] = __builtin_amdgcn_readfirstlane((hg + 1) * (int)head_bytes);
+      l_r[2] = d_r[2] = __builtin_amdgcn_readfirstlane((hg + 1) * N * 4);
     }
     const unsigned so = rg_a + (i % kStages) * C::STAGE;
 #pragma unroll
@@ -225,8 +232,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       const unsigned off = (unsigned)(kw0 + kb * 32 + l32) * C::RB + kk * 32 + hh * 16;
       vf[kb][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
-  issue_qtile(0);
-  issue_qtile(1);
+  issue_qtile(0, 0);
+  issue_qtile(1, GQA ? (nt == 1 ? 1 : 0) : 0);
 
   // ---- per-lane LDS addresses (byte offsets; chunk bits XORed per step).
   // Rows of a 32-row block read with lanes = one row each (Q, dO: permuted).
@@ -281,9 +288,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // `visit`, at the rows' own offsets in rdq. A tile that does not exist (or
   // rows past N) gets offsets past the buffer: the operations are no-ops, so
   // the number of memory operations per tile is the same everywhere.
-  auto dq_atomic = [&](const f32x16& acc, int visit, bool live, int r) INL {
-    const int q = vtile(visit) * kBR + 8 * (r >> 2) + 4 * hh + (r & 3);
-    const unsigned off = live && q < N ? ((unsigned)(vhead(visit) * N + q) * D + db_q * 32 + l32) * 4 : 0x80000000u;
+  auto dq_atomic = [&](const f32x16& acc, int visit, int vq, bool live, int r) INL {
+    const int q = vtile(visit, vq) * kBR + 8 * (r >> 2) + 4 * hh + (r & 3);
+    const unsigned off = live && q < N ? ((unsigned)(vhead(visit, vq) * N + q) * D + db_q * 32 + l32) * 4 : 0x80000000u;
     if constexpr (DET) {
       // (Bit cast of a copy: hipcc compiled a bit cast applied directly to an
       // element of a vector variable as a cast of its first element.)
@@ -294,9 +301,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     }
   };
   constexpr int NDQ = 16;   // dQ memory operations per visit
-  auto dq_atomics = [&](const f32x16& acc, int visit, bool live) INL {
+  auto dq_atomics = [&](const f32x16& acc, int visit, int vq, bool live) INL {
 #pragma unroll
-    for (int r = 0; r < NDQ; ++r) dq_atomic(acc, visit, live, r);
+    for (int r = 0; r < NDQ; ++r) dq_atomic(acc, visit, vq, live, r);
   };
 
   __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS));   // K tile, V operands, query tile 0
@@ -309,7 +316,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // i % 3; its dS^T goes to dS buffer i % 2, which dQ of visit i reads during
   // visit i + 1.
   for (int i = 0; i < nvis; ++i) {
-    const int qt = vtile(i);
+    // head (quotient by nt) of visits i, i - 1 and i + 2
+    const int iq = GQA ? i / nt : 0;
+    const int iq_prev = GQA ? (i - iq * nt == 0 ? iq - 1 : iq) : 0;
+    const int iq_next = GQA ? (i + 2 - iq * nt >= 2 * nt ? iq + 2 : i + 2 - iq * nt >= nt ? iq + 1 : iq) : 0;
+    const int qt = vtile(i, iq);
     if (i > 0) {
       // Memory operations issued after visit i's own copies: (i >= 2) the NDQ
       // dQ operations of visit i-2, then the copies of visit i+1 and the NDQ
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       // Copies of visit i+2 go to the stage of visit i-1 (free since the
       // barrier). Issued here rather than right after the barrier, where
       // they would queue behind the previous visit's dQ atomics and stall.
-      if (kb == 1) issue_qtile(i + 2);
+      if (kb == 1) issue_qtile(i + 2, iq_next);
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
       if (kb == 1) ldv[0] = rd_ld(0);
@@ -480,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
         constexpr int NA = NS - QS;
         const int lo = (step - QS) * NDQ / NA, hi = (step - QS + 1) * NDQ / NA;
 #pragma unroll
-        for (int r = lo; r < hi; ++r) dq_atomic(dq_acc, i - 1, i > 0, r);
+        for (int r = lo; r < hi; ++r) dq_atomic(dq_acc, i - 1, iq_prev, i > 0, r);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -501,10 +512,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       dq_acc = mma(join(qop[m % 3].v[0], qop[m % 3].v[1]), join(qop[m % 3].v[2], qop[m % 3].v[3]), dq_acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    dq_atomics(dq_acc, nvis - 1, true);
+    dq_atomics(dq_acc, nvis - 1, G - 1, true);
   }
 
   // Epilogue: dK = scale * acc, dV = acc (lanes = d, rows = keys); rows past N dropped.
+  if (a.dkv_part != nullptr) {
+    // float32 dK and dV of this chunk: [batch, K/V head][chunk][N][d] each.
+    const size_t pb = ((size_t)bh * a.hchunks + chunk) * (size_t)N * D;
+    const size_t half = (size_t)(a.H / a.group) * a.hchunks * (size_t)N * D * (size_t)(a.B);
+    const __amdgpu_buffer_rsrc_t rpk = make_rsrc(a.dkv_part + pb, (unsigned)N * D * 4);
+    const __amdgpu_buffer_rsrc_t rpv = make_rsrc(a.dkv_part + half + pb, (unsigned)N * D * 4);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kw0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const unsigned off = ((unsigned)key * D + db * 32 + l32) * 4;
+          const float kx = dk[kb][db][r] * a.scale, vx = dv[kb][db][r];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, kx), rpk, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, vx), rpv, off, 0, 0);
+        }
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    return;
+  }
   const __amdgpu_buffer_rsrc_t rdk = make_rsrc((__bf16*)a.dk + base, head_bytes);
   const __amdgpu_buffer_rsrc_t rdv = make_rsrc((__bf16*)a.dv + base, head_bytes);
   const float scale = a.scale;
@@ -531,7 +563,7 @@ template <int D, bool CAUSAL, bool DET>
 void launch_main(const BwdArgs& a, long long grid, hipStream_t s) {
   if constexpr (DET)
     hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
-  else if (a.group > 1)
+  else if (a.group > a.hchunks)   // several query heads per workgroup
     hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, false, false>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -542,7 +574,7 @@ void launch_main(const BwdArgs& a, long long grid, hipStream_t s) {
 hipError_t launch_bwd_bf16_main(int d, int causal, BwdArgs a, int B, int H, hipStream_t s) {
   a.n_tiles = (a.N + kBC - 1) / kBC;
   // One workgroup per (batch, K/V head, key tile).
-  const long long grid = (long long)B * (H / a.group) * a.n_tiles;
+  const long long grid = (long long)B * (H / a.group) * a.hchunks * a.n_tiles;
   a.remap = grid % 8 == 0 ? 1 : 0;
   const bool det = a.dq_part != nullptr;
   if (d == 64) {

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -186,7 +186,7 @@ def test_gqa_rejects(lib):
 
     def bwd(H=4, H_kv=2, N=16, d=64, ws_bytes=None):
         if ws_bytes is None:
-            ws_bytes = lib.fa_bwd_workspace_bytes(1, H, N, d)
+            ws_bytes = max(lib.fa_bwd_gqa_workspace_bytes(1, H, max(H_kv, 1), N, d), 1 << 20)
         return lib.fa_bwd_gqa(A, A + GAP, A + 2 * GAP, A + 3 * GAP, A + 4 * GAP, A + 5 * GAP, A + 6 * GAP,
                               A + 7 * GAP, A + 8 * GAP, A + 10 * GAP, ws_bytes, 1, H, H_kv, N, d, 0.125, 1, None)
 
@@ -198,6 +198,31 @@ def test_gqa_rejects(lib):
     assert fwd(o=A + 256) == _lib.FA_ERR_INVALID          # o overlaps q
     assert fwd(o=A + GAP + 64) == _lib.FA_ERR_INVALID     # o inside k
     assert bwd(ws_bytes=100) == _lib.FA_ERR_INVALID
-    # a group's dQ rows must fit 32-bit offsets: 64 heads x N = 2^17 x 64 x 4 bytes
-    assert bwd(H=64, H_kv=1, N=1 << 17, d=64) == _lib.FA_ERR_UNSUPPORTED
+    # the dQ rows of a workgroup's query heads must fit 32-bit offsets: at N = 2^21
+    # there are 8192 key tiles, so the 8 heads of the group stay in one chunk
+    # (8 x 2^21 x 64 x 4 bytes = 2^32)
+    assert bwd(H=8, H_kv=1, N=1 << 21, d=64) == _lib.FA_ERR_UNSUPPORTED
     assert "group too large" in lib.fa_last_error().decode()
+
+
+def test_gqa_workspace(lib):
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    def chunks(B, H, H_kv, N):
+        G, base = H // H_kv, B * H_kv * -(-N // 256)
+        return next((c for c in range(1, G) if G % c == 0 and base * c >= 2048), G)
+
+    for (B, H, H_kv, N, d) in [(1, 32, 8, 16384, 128), (1, 32, 1, 16384, 128), (8, 32, 8, 16384, 128),
+                               (2, 6, 3, 100, 64), (1, 4, 4, 300, 128)]:
+        got = lib.fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, d)
+        base = lib.fa_bwd_workspace_bytes(B, H, N, d)
+        c = chunks(B, H, H_kv, N) if H_kv < H else 1
+        assert got == base + (al(2 * B * H_kv * c * N * d * 4) if c > 1 else 0), (B, H, H_kv, N, d)
+    # one K/V head of 32 query heads at N = 16384: 32 chunks (one head each, 2048 workgroups)
+    assert lib.fa_bwd_gqa_workspace_bytes(1, 32, 1, 16384, 128) == \
+        lib.fa_bwd_workspace_bytes(1, 32, 16384, 128) + 2 * 32 * 16384 * 128 * 4
+    # enough workgroups without splitting: no extra space
+    assert lib.fa_bwd_gqa_workspace_bytes(8, 32, 8, 16384, 128) == lib.fa_bwd_workspace_bytes(8, 32, 16384, 128)
+    assert lib.fa_bwd_gqa_workspace_bytes(1, 6, 4, 100, 64) == 0
+    assert lib.fa_bwd_gqa_workspace_bytes(1, 6, 0, 100, 64) == 0

@@ -123,3 +123,32 @@ def test_gqa_long_context_sampled_heads(fa):
     grp = slice(j * G, (j + 1) * G)
     ref = A.backward_gqa(x["q"][:, grp], sl(x["k"], j), sl(x["v"], j), x["do"][:, grp], w.scale, True)
     _check_grads([dq[:, grp], dk[:, j:j + 1], dv[:, j:j + 1]], ref, "gqa H=32/4 N=4096 group 1")
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d,chunks", [
+    (64, 4, 2, 4096, 64, 1),    # 2048 workgroups unsplit: each sums its 2 heads in registers
+    (64, 8, 1, 2048, 128, 4),   # 4 chunks of 2 heads: registers, then the fixed-order chunk sum
+])
+def test_gqa_head_chunks(fa, B, H, H_kv, N, d, chunks):
+    """Groups summed in one workgroup, and groups split into multi-head
+    chunks: sampled batches against the oracle, dK/dV bits repeatable."""
+    import torch
+    base = fa.bwd_workspace_bytes(B, H, N, d)
+    extra = 2 * B * H_kv * chunks * N * d * 4 if chunks > 1 else 0
+    assert fa.bwd_gqa_workspace_bytes(B, H, H_kv, N, d) == base + extra   # the split under test
+    w, x, (q, k, v, do) = _inputs(1900 + H, B, H, H_kv, N, d, True)
+    announce(f"fa_bwd_gqa chunks={chunks} B={B} H={H} H_kv={H_kv} N={N} d={d}")
+    o, lse = fa.fwd(q, k, v, causal=True)
+    g1 = fa.bwd(q, k, v, o, lse, do, causal=True)
+    g2 = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(g1[1:], g2[1:]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    dq, dk, dv = (host(t) for t in g1)
+    G = H // H_kv
+    for b, j in ((3, H_kv - 1), (B - 1, 0)):
+        grp = slice(j * G, (j + 1) * G)
+        ref = A.backward_gqa(x["q"][b:b + 1, grp], x["k"][b:b + 1, j:j + 1], x["v"][b:b + 1, j:j + 1],
+                             x["do"][b:b + 1, grp], w.scale, True)
+        _check_grads([dq[b:b + 1, grp], dk[b:b + 1, j:j + 1], dv[b:b + 1, j:j + 1]], ref,
+                     f"gqa chunks={chunks} batch {b} K/V head {j}")
