@@ -187,11 +187,11 @@ def gqa_section(fa, steps: int, warmup: int, H_kv_list=(8, 1)):
     q, do = mk(H), mk(H)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
-    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), device="cuda", dtype=torch.uint8)
     dq = torch.empty_like(q)
     res = {}
     for H_kv in H_kv_list:
         k, v = mk(H_kv), mk(H_kv)
+        ws = torch.empty(fa.bwd_gqa_workspace_bytes(B, H, H_kv, N, d), device="cuda", dtype=torch.uint8)
         dk, dv = torch.empty_like(k), torch.empty_like(v)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
 
@@ -218,7 +218,7 @@ def gqa_section(fa, steps: int, warmup: int, H_kv_list=(8, 1)):
                                "fwd_tflops": round(ff / (f_ms * 1e-3) / 1e12, 2),
                                "bwd_tflops": round(fb / (b_ms * 1e-3) / 1e12, 2),
                                "tflops": round((ff + fb) / ((f_ms + b_ms) * 1e-3) / 1e12, 2)}
-        del k, v, dk, dv
+        del k, v, dk, dv, ws
     return {"workload": f"grouped-query causal bf16 attention, B={B} H={H} N={N} d={d}, fwd + bwd", **res}
 
 
