@@ -40,7 +40,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["scores", "safe_softmax", "forward", "backward", "forward_rows",
-           "backward_head", "kv_head", "forward_gqa", "backward_gqa"]
+           "backward_head", "kv_head", "forward_gqa", "backward_gqa", "forward_varlen",
+           "backward_varlen"]
 
 
 def _f64(x) -> np.ndarray:
@@ -248,4 +249,59 @@ def backward_gqa(q, k, v, do, scale: float, causal: bool = False, row_chunk: int
             dq[b, h], dk_h, dv_h = backward_head(q[b, h], k[b, j], v[b, j], do[b, h], scale, causal, row_chunk)
             dk[b, j] += dk_h
             dv[b, j] += dv_h
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Variable-length batches packed along the sequence axis.
+#
+# "FlashAttention v1～v4 完整进化史" (v4 part 4) names variable-length
+# sequences as a source of load imbalance, and its closing checklist lists
+# them among backend features, without a layout. Reading: B sequences of
+# lengths n_b are packed one after another, rows cu[b] .. cu[b+1]-1 of every
+# head (cu = cumulative lengths, cu[0] = 0, cu[B] = T), q, o [H, T, d] and
+# k, v [H_kv, T, d]; a query attends only to the keys of its own sequence
+# (and, causal, to those at or before its own position in it). Heads map to
+# K/V heads as in forward_gqa.
+
+
+def forward_varlen(q, k, v, cu_seqlens, scale: float, causal: bool = False, row_chunk: int = 1024):
+    """(O [H, T, d], LSE [H, T]) of packed sequences."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = [int(x) for x in cu_seqlens]
+    H, T, _ = q.shape
+    H_kv = k.shape[0]
+    o = np.zeros(q.shape[:-1] + (v.shape[-1],), dtype=np.float64)
+    lse = np.full((H, T), -np.inf, dtype=np.float64)
+    for b in range(len(cu) - 1):
+        r0, r1 = cu[b], cu[b + 1]
+        if r1 <= r0:
+            continue
+        for h in range(H):
+            j = kv_head(h, H, H_kv)
+            o[h, r0:r1], lse[h, r0:r1] = _head_forward(q[h, r0:r1], k[j, r0:r1], v[j, r0:r1], scale, causal,
+                                                       row_chunk)
+    return o, lse
+
+
+def backward_varlen(q, k, v, do, cu_seqlens, scale: float, causal: bool = False, row_chunk: int = 1024):
+    """(dQ [H, T, d], dK, dV [H_kv, T, d]) of packed sequences; dK, dV of a
+    shared K/V head sum its query heads in ascending order."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    cu = [int(x) for x in cu_seqlens]
+    H = q.shape[0]
+    H_kv = k.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(len(cu) - 1):
+        r0, r1 = cu[b], cu[b + 1]
+        if r1 <= r0:
+            continue
+        for h in range(H):
+            j = kv_head(h, H, H_kv)
+            g = backward_head(q[h, r0:r1], k[j, r0:r1], v[j, r0:r1], do[h, r0:r1], scale, causal, row_chunk)
+            dq[h, r0:r1] = g[0]
+            dk[j, r0:r1] += g[1]
+            dv[j, r0:r1] += g[2]
     return dq, dk, dv
