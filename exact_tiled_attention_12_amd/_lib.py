@@ -33,6 +33,11 @@ SIGNATURES = {
     "fa_bwd_gqa": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
     "fa_bwd_gqa_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "fa_fwd_varlen": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                               _c_float, _c_int, _p]),
+    "fa_bwd_varlen": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size, _p,
+                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
+    "fa_bwd_varlen_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "fa_bwd_det": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
     "fa_bwd_det_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),

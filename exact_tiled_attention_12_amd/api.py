@@ -13,7 +13,7 @@ import torch
 from . import _lib
 
 __all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "bwd_det_workspace_bytes", "bwd_gqa_workspace_bytes",
-           "quant_fp8", "fwd_fp8"]
+           "fwd_varlen", "bwd_varlen", "quant_fp8", "fwd_fp8"]
 
 
 def _stream(t: torch.Tensor):
@@ -85,6 +85,73 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
             B, H, N, d, float(scale), int(bool(causal)), _stream(q))
     _lib.check(st, "fa_fwd" if dt == torch.bfloat16 else "fa_fwd_f32")
     return out, lse
+
+
+def _check_cu(cu_seqlens, device):
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-D int32 tensor of cumulative sequence lengths")
+    if cu_seqlens.device != device or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous on the tensors' device")
+    return int(cu_seqlens.numel()) - 1
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
+               out=None, lse=None):
+    """Packed variable-length attention: q [H, T, d], k, v [H_kv, T, d] (bf16);
+    sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1. Returns O [H, T, d]
+    and LSE [H, T]."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("fwd_varlen takes [H, T, d] tensors")
+    H, T, d = (int(x) for x in q.shape)
+    H_kv = int(k.shape[0])
+    n_seq = _check_cu(cu_seqlens, q.device)
+    _check_tensor(q, "q", torch.bfloat16, (H, T, d))
+    for t, n in ((k, "k"), (v, "v")):
+        _check_tensor(t, n, torch.bfloat16, (H_kv, T, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, T), device=q.device, dtype=torch.float32) if lse is None else lse
+    _check_tensor(out, "out", torch.bfloat16, (H, T, d))
+    _check_tensor(lse, "lse", torch.float32, (H, T))
+    st = _lib.load().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                   cu_seqlens.data_ptr(), n_seq, int(max_seqlen), T, H, H_kv, d, float(scale),
+                                   int(bool(causal)), _stream(q))
+    _lib.check(st, "fa_fwd_varlen")
+    return out, lse
+
+
+def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, causal: bool = False,
+               scale: float | None = None, workspace=None, dq=None, dk=None, dv=None):
+    """Gradients of fwd_varlen: dQ [H, T, d], dK, dV [H_kv, T, d] (bf16)."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("bwd_varlen takes [H, T, d] tensors")
+    H, T, d = (int(x) for x in q.shape)
+    H_kv = int(k.shape[0])
+    n_seq = _check_cu(cu_seqlens, q.device)
+    for t, n in ((q, "q"), (o, "o"), (do, "do")):
+        _check_tensor(t, n, torch.bfloat16, (H, T, d))
+    for t, n in ((k, "k"), (v, "v")):
+        _check_tensor(t, n, torch.bfloat16, (H_kv, T, d))
+    _check_tensor(lse, "lse", torch.float32, (H, T))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = _lib.load()
+    if workspace is None:
+        workspace = torch.empty(int(lib.fa_bwd_varlen_workspace_bytes(T, H, H_kv, d)), device=q.device,
+                                dtype=torch.uint8)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_tensor(dq, "dq", torch.bfloat16, (H, T, d))
+    for t, n in ((dk, "dk"), (dv, "dv")):
+        _check_tensor(t, n, torch.bfloat16, (H_kv, T, d))
+    st = lib.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), cu_seqlens.data_ptr(), n_seq,
+                           int(max_seqlen), T, H, H_kv, d, float(scale), int(bool(causal)), _stream(q))
+    _lib.check(st, "fa_bwd_varlen")
+    return dq, dk, dv
 
 
 def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:

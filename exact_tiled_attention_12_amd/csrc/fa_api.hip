@@ -240,6 +240,77 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
                     scale, causal, stream, 7, false, H_kv);
 }
 
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
+                  int n_seq, int max_seqlen, int total, int H, int H_kv, int d, float scale, int causal,
+                  void* stream) {
+  int rc = check_shape(1, H, total, d, scale);
+  if (rc) return rc;
+  if (H_kv < 1) return check_kv_heads(H, H_kv);
+  rc = check_kv_heads(H, H_kv);
+  if (rc) return rc;
+  if (n_seq < 1 || max_seqlen < 1 || max_seqlen > total)
+    return fail(FA_ERR_INVALID, "need n_seq >= 1 and 1 <= max_seqlen <= total (got n_seq=%d max_seqlen=%d total=%d)",
+                n_seq, max_seqlen, total);
+  if ((long long)n_seq * H * ((max_seqlen + 255) / 256) > INT_MAX / 2)
+    return fail(FA_ERR_UNSUPPORTED, "too many sequences: n_seq = %d", n_seq);
+  const size_t tb = (size_t)H * total * d * 2, kb = (size_t)H_kv * total * d * 2, lb = (size_t)H * total * 4;
+  const Buf in[4] = {{q, tb, "q", 16}, {k, kb, "k", 16}, {v, kb, "v", 16},
+                     {cu_seqlens, (size_t)(n_seq + 1) * 4, "cu_seqlens", 4}};
+  const Buf out[2] = {{o, tb, "o", 16}, {lse, lb, "lse", 4}};
+  rc = check_bufs(in, 4, out, 2);
+  if (rc) return rc;
+  fa::FwdArgs a{q, k, v, o, lse, total, 0, log2e_scale(scale), 0, H, H / H_kv, cu_seqlens, max_seqlen};
+  return launched(fa::launch_fwd(fa::DType::BF16, d, causal, a, n_seq, H, (hipStream_t)stream),
+                  "variable-length attention forward");
+}
+
+size_t fa_bwd_varlen_workspace_bytes(int total, int H, int H_kv, int d) {
+  const size_t base = fa_bwd_workspace_bytes(1, H, total, d);
+  if (base == 0 || H_kv < 1 || H_kv > H || H % H_kv != 0) return 0;
+  // grouped heads: float32 dK, dV per query head, [H_kv][G][total][d] each
+  return H_kv < H ? base + align256((size_t)2 * H * total * d * 4) : base;
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, const int* cu_seqlens,
+                  int n_seq, int max_seqlen, int total, int H, int H_kv, int d, float scale, int causal,
+                  void* stream) {
+  int rc = check_shape(1, H, total, d, scale);
+  if (rc) return rc;
+  if (H_kv < 1) return check_kv_heads(H, H_kv);
+  rc = check_kv_heads(H, H_kv);
+  if (rc) return rc;
+  if (n_seq < 1 || max_seqlen < 1 || max_seqlen > total)
+    return fail(FA_ERR_INVALID, "need n_seq >= 1 and 1 <= max_seqlen <= total (got n_seq=%d max_seqlen=%d total=%d)",
+                n_seq, max_seqlen, total);
+  if ((long long)n_seq * H * ((max_seqlen + 255) / 256) > INT_MAX / 2)
+    return fail(FA_ERR_UNSUPPORTED, "too many sequences: n_seq = %d", n_seq);
+  const size_t need = fa_bwd_varlen_workspace_bytes(total, H, H_kv, d);
+  if (workspace == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(FA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID, "workspace has %zu bytes, needs fa_bwd_varlen_workspace_bytes() = %zu",
+                workspace_bytes, need);
+  const size_t tb = (size_t)H * total * d * 2, kb = (size_t)H_kv * total * d * 2, lb = (size_t)H * total * 4;
+  const Buf in[7] = {{q, tb, "q", 16},   {k, kb, "k", 16},    {v, kb, "v", 16},
+                     {o, tb, "o", 16},   {lse, lb, "lse", 4}, {dout, tb, "dout", 16},
+                     {cu_seqlens, (size_t)(n_seq + 1) * 4, "cu_seqlens", 4}};
+  const Buf out[4] = {{dq, tb, "dq", 16}, {dk, kb, "dk", 16}, {dv, kb, "dv", 16}, {workspace, need, "workspace", 256}};
+  rc = check_bufs(in, 7, out, 4);
+  if (rc) return rc;
+  fa::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.N = total; a.scale = scale; a.c = log2e_scale(scale);
+  a.H = H; a.group = H / H_kv; a.hchunks = H / H_kv; a.B = 1;
+  a.cu_seqlens = cu_seqlens; a.n_seq = n_seq; a.max_seqlen = max_seqlen;
+  a.dq_acc = (float*)workspace;
+  a.dvec = (float*)((char*)workspace + align256((size_t)H * total * d * 4));
+  if (H_kv < H) a.dkv_part = (float*)((char*)workspace + fa_bwd_workspace_bytes(1, H, total, d));
+  return launched(fa::launch_bwd(fa::DType::BF16, d, causal, a, 1, H, 7, (hipStream_t)stream),
+                  "variable-length attention backward");
+}
+
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
                const float* dout, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, int B,
                int H, int N, int d, float scale, int causal, void* stream) {

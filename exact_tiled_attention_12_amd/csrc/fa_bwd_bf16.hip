@@ -113,9 +113,15 @@ __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
 // DET: dQ contributions go to partial tiles (plain stores, one tile per
 // visited (key tile, query tile) pair) instead of float32 atomics.
 // GQA: the key tile belongs to a K/V head shared by a.group consecutive query
-// heads; the workgroup visits the query tiles of each of them in turn, so
-// dK and dV sum over the group in registers (a.group == 1 without GQA).
-template <int D, bool CAUSAL, bool DET, bool GQA>
+// heads, split into a.hchunks chunks; the workgroup of a chunk of several heads
+// visits the query tiles of each of them in turn, so dK and dV sum over the
+// chunk in registers. (Chunks of one head run the GQA = false kernel.) With
+// more than one chunk, each chunk's float32 dK and dV go to the workspace
+// for a fixed-order sum over chunks.
+// VARLEN: packed variable-length batch, one workgroup per (sequence, query
+// head, key tile) with the sequence's rows and length; key tiles past the
+// sequence's end exit at once.
+template <int D, bool CAUSAL, bool DET, bool GQA, bool VARLEN = false>
 __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // Device pass only (the host pass needs just the launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -135,20 +141,44 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
   int wg = blockIdx.x;
   if (a.remap) wg = xcd_remap(wg, gridDim.x);
-  const int bhc = wg / a.n_tiles;           // (batch, K/V head, chunk)
+  const int bhc = wg / a.n_tiles;           // (batch, K/V head, chunk), or (sequence, query head)
   const int kt = wg - bhc * a.n_tiles;       // key tile; tile 0 (heaviest when causal) first
-  const int N = a.N;
   // (batch, K/V head) and the chunk of its query heads. Without GQA a chunk
   // is one query head (bhc is the query head); a.group > 1 then means grouped
   // query heads handled one per workgroup.
-  const int bh = GQA ? bhc / a.hchunks : (a.group == 1 ? bhc : bhc / a.group);
-  const int chunk = bhc - bh * (GQA ? a.hchunks : a.group);
+  int N, bh, chunk;
+  size_t base, qbase, lbase, pbase;   // K/V rows, query rows, L/D rows, float32 dK/dV partial rows
   const int G = GQA ? a.group / a.hchunks : 1;         // query heads this workgroup visits
-  // First query head of the chunk (the query heads of K/V head j of batch b
-  // are b H + j group .. b H + j group + group - 1).
-  const int qh0 = GQA ? (bh / (a.H / a.group)) * a.H + (bh % (a.H / a.group)) * a.group + chunk * G : bhc;
-  const size_t base = (size_t)bh * (size_t)N * D;
-  const size_t qbase = (size_t)qh0 * (size_t)N * D;
+  if constexpr (VARLEN) {
+    // Rows cu[seq] .. cu[seq+1]-1 of every head (T = a.N rows per head);
+    // clamped to the packed tensor and to max_seqlen, so that malformed
+    // lengths stay inside the buffers.
+    const int T = a.N;
+    const int seq = bhc / a.H, h = bhc - seq * a.H;
+    int s0 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq]);
+    int s1 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]);
+    s0 = min(max(s0, 0), T);
+    s1 = min(max(s1, s0), T);
+    N = min(s1 - s0, a.max_seqlen);
+    if (kt * kBC >= N) return;   // uniform: the key tile lies past the sequence
+    bh = h / a.group;
+    chunk = h - bh * a.group;
+    base = ((size_t)bh * T + s0) * D;
+    qbase = ((size_t)h * T + s0) * D;
+    lbase = (size_t)h * T + s0;
+    pbase = (((size_t)bh * a.group + chunk) * T + s0) * D;
+  } else {
+    N = a.N;
+    bh = GQA ? bhc / a.hchunks : (a.group == 1 ? bhc : bhc / a.group);
+    chunk = bhc - bh * (GQA ? a.hchunks : a.group);
+    // First query head of the chunk (the query heads of K/V head j of batch b
+    // are b H + j group .. b H + j group + group - 1).
+    const int qh0 = GQA ? (bh / (a.H / a.group)) * a.H + (bh % (a.H / a.group)) * a.group + chunk * G : bhc;
+    base = (size_t)bh * (size_t)N * D;
+    qbase = (size_t)qh0 * (size_t)N * D;
+    lbase = (size_t)qh0 * N;
+    pbase = ((size_t)bh * a.hchunks + chunk) * (size_t)N * D;
+  }
   const unsigned head_bytes = (unsigned)N * C::RB;
   // Query-side buffers start at the group's first head; a visit to head g of
   // the group shifts its offsets by g heads and ends its buffer at head g's
@@ -156,8 +186,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   const i32x4 rq = dma_rsrc((const __bf16*)a.q + qbase, head_bytes);
   const i32x4 rk = dma_rsrc((const __bf16*)a.k + base, head_bytes);
   const i32x4 rg = dma_rsrc((const __bf16*)a.dout + qbase, head_bytes);
-  const i32x4 rl = dma_rsrc(a.lse + (size_t)qh0 * N, (unsigned)N * 4);
-  const i32x4 rd = dma_rsrc(a.dvec + (size_t)qh0 * N, (unsigned)N * 4);
+  const i32x4 rl = dma_rsrc(a.lse + lbase, (unsigned)N * 4);
+  const i32x4 rd = dma_rsrc(a.dvec + lbase, (unsigned)N * 4);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + base, head_bytes);
 
   const int k0 = kt * kBC;
@@ -517,9 +547,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
   // Epilogue: dK = scale * acc, dV = acc (lanes = d, rows = keys); rows past N dropped.
   if (a.dkv_part != nullptr) {
-    // float32 dK and dV of this chunk: [batch, K/V head][chunk][N][d] each.
-    const size_t pb = ((size_t)bh * a.hchunks + chunk) * (size_t)N * D;
-    const size_t half = (size_t)(a.H / a.group) * a.hchunks * (size_t)N * D * (size_t)(a.B);
+    // float32 dK and dV of this chunk: [batch, K/V head][chunk][N][d] each
+    // (VARLEN: [K/V head][chunk][T][d], this sequence's rows).
+    const size_t pb = pbase;
+    const size_t half = (size_t)(a.H / a.group) * a.hchunks * (size_t)a.N * D * (size_t)(a.B);
     const __amdgpu_buffer_rsrc_t rpk = make_rsrc(a.dkv_part + pb, (unsigned)N * D * 4);
     const __amdgpu_buffer_rsrc_t rpv = make_rsrc(a.dkv_part + half + pb, (unsigned)N * D * 4);
 #pragma unroll
@@ -561,7 +592,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
 template <int D, bool CAUSAL, bool DET>
 void launch_main(const BwdArgs& a, long long grid, hipStream_t s) {
-  if constexpr (DET)
+  if (a.cu_seqlens != nullptr)   // packed variable-length batch, one query head per workgroup
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, false, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if constexpr (DET)
     hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (a.group > a.hchunks)   // several query heads per workgroup
     hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -572,9 +605,12 @@ void launch_main(const BwdArgs& a, long long grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd_bf16_main(int d, int causal, BwdArgs a, int B, int H, hipStream_t s) {
-  a.n_tiles = (a.N + kBC - 1) / kBC;
-  // One workgroup per (batch, K/V head, key tile).
-  const long long grid = (long long)B * (H / a.group) * a.hchunks * a.n_tiles;
+  // One workgroup per (batch, K/V head, head chunk, key tile), or, for a
+  // packed variable-length batch, per (sequence, query head, key tile of the
+  // longest sequence).
+  a.n_tiles = ((a.cu_seqlens != nullptr ? a.max_seqlen : a.N) + kBC - 1) / kBC;
+  const long long grid = a.cu_seqlens != nullptr ? (long long)a.n_seq * H * a.n_tiles
+                                                 : (long long)B * (H / a.group) * a.hchunks * a.n_tiles;
   a.remap = grid % 8 == 0 ? 1 : 0;
   const bool det = a.dq_part != nullptr;
   if (d == 64) {

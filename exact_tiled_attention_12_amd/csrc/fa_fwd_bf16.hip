@@ -109,7 +109,9 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int D, bool CAUSAL>
+// VARLEN: packed variable-length batch; a workgroup of a tile past its
+// sequence's end exits at once.
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // The body is compiled in the device pass only: the host pass needs just the
   // launch stub, and its front end drops the stub of a kernel whose lambdas
@@ -140,15 +142,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   int wg = blockIdx.x;
   if (a.remap) wg = xcd_remap(wg, gridDim.x);
-  const int bh = wg / a.n_qtiles;
+  const int bh = wg / a.n_qtiles;   // (batch, head), or (sequence, head) for VARLEN
   const int t = wg - bh * a.n_qtiles;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - t) : t;
-  const int N = a.N;
-  const size_t base = (size_t)bh * (size_t)N * D;
-  // K/V head of this query head: groups of `group` consecutive query heads
-  // share one (grouped-query attention; group = 1 is one K/V head per head).
-  const int kvh = a.group == 1 ? bh : (bh / a.H) * (a.H / a.group) + (bh % a.H) / a.group;
-  const size_t kv_base = (size_t)kvh * (size_t)N * D;
+  int N = a.N;
+  size_t base, kv_base, lse_base;
+  if constexpr (VARLEN) {
+    // Rows cu[seq] .. cu[seq+1]-1 of every head; clamped to the packed
+    // tensor and to the longest-sequence bound, so that malformed lengths
+    // stay inside the buffers.
+    const int seq = bh / a.H, h = bh - seq * a.H;
+    int s0 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq]);
+    int s1 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]);
+    s0 = min(max(s0, 0), a.N);
+    s1 = min(max(s1, s0), a.N);
+    N = min(s1 - s0, a.n_qtiles * kBR);
+    if (qt * kBR >= N) return;   // uniform: the tile lies past the sequence
+    const int kvh = h / a.group;
+    base = ((size_t)h * a.N + s0) * D;
+    kv_base = ((size_t)kvh * a.N + s0) * D;
+    lse_base = (size_t)h * a.N + s0;
+  } else {
+    base = (size_t)bh * (size_t)N * D;
+    // K/V head of this query head: groups of `group` consecutive query heads
+    // share one (grouped-query attention; group = 1 is one K/V head per head).
+    const int kvh = a.group == 1 ? bh : (bh / a.H) * (a.H / a.group) + (bh % a.H) / a.group;
+    kv_base = (size_t)kvh * (size_t)N * D;
+    lse_base = (size_t)bh * N;
+  }
   const unsigned head_bytes = (unsigned)N * C::RB;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)a.q + base, head_bytes);
   const i32x4 rk = dma_rsrc((const __bf16*)a.k + kv_base, head_bytes);
@@ -448,14 +469,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
         w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
         *(u32x2*)(og + db * 32 + 8 * g + 4 * hh) = w;
       }
-    if (hh == 0) a.lse[(size_t)bh * N + qrow] = lt == 0.f ? -INFINITY : (m_ref + fast_log2(lt)) * kLn2;
+    if (hh == 0) a.lse[lse_base + qrow] = lt == 0.f ? -INFINITY : (m_ref + fast_log2(lt)) * kLn2;
   }
 #endif
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, s, a);
+  if (a.cu_seqlens != nullptr)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -466,7 +490,9 @@ hipError_t launch_fwd_bf16(int d, int causal, FwdArgs a, int B, int H, hipStream
   // zero scale becomes the smallest normal float, whose products with any
   // finite score round exp2 to 1 exactly as scale 0 would.
   a.c = fmaxf(a.c, FLT_MIN);
-  a.n_qtiles = (a.N + kBR - 1) / kBR;
+  // Packed variable-length batch: B sequences, tiles of the longest; one
+  // workgroup per (sequence, head, tile).
+  a.n_qtiles = ((a.cu_seqlens != nullptr ? a.max_seqlen : a.N) + kBR - 1) / kBR;
   const long long grid = (long long)B * H * a.n_qtiles;
   a.remap = (grid % 8 == 0) ? 1 : 0;
   if (d == 64) return causal ? launch<64, true>(a, (int)grid, s) : launch<64, false>(a, (int)grid, s);

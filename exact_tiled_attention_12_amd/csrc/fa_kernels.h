@@ -20,6 +20,11 @@ struct FwdArgs {
   int remap;      // filled by the launcher
   int H;          // query heads
   int group;      // query heads per K/V head (1 unless grouped-query, bf16 only)
+  // Packed variable-length batch (bf16): cumulative sequence lengths
+  // [n_seq + 1], or nullptr. N is then the packed length T (the row stride of
+  // a head) and n_qtiles the tiles of the longest sequence.
+  const int* cu_seqlens;
+  int max_seqlen;
 };
 
 struct BwdArgs {
@@ -45,6 +50,12 @@ struct BwdArgs {
   int hchunks;    // grouped-query: workgroups (head chunks) per K/V head and key tile
   int B;          // batch
   float* dkv_part;  // grouped-query with hchunks > 1: float32 dK, dV per chunk, else nullptr
+  // Packed variable-length batch: cumulative sequence lengths [B + 1], or
+  // nullptr. N is then the packed length T (the row stride of a head; B = 1
+  // for the streaming passes) and max_seqlen bounds every sequence.
+  const int* cu_seqlens;
+  int n_seq;
+  int max_seqlen;
 };
 
 // Grouped-query backward: chunks of each K/V head's query heads, one

@@ -137,6 +137,42 @@ FA_API int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o
  * Returns 0 for invalid sizes. */
 FA_API size_t fa_bwd_gqa_workspace_bytes(int B, int H, int H_kv, int N, int d);
 
+/* Packed variable-length batches, bf16 ("FlashAttention v1～v4 完整进化史",
+ * v4 part 4: variable-length sequences, with causal masks, make the work per
+ * tile uneven, and heavier tiles are scheduled first). n_seq sequences are
+ * packed along the sequence axis: sequence b is rows cu_seqlens[b] ..
+ * cu_seqlens[b+1]-1 of every head. q, o: [H, total, d]; k, v: [H_kv, total, d]
+ * (H a multiple of H_kv, grouping as in fa_fwd_gqa); lse: [H, total] float32.
+ * A query attends only to the keys of its own sequence (causal: those at or
+ * before its position in it). cu_seqlens: DEVICE int32 [n_seq + 1],
+ * non-decreasing from 0 to total, every length at most max_seqlen; it is read
+ * by the kernels only (the library never synchronises), which clamp each
+ * sequence to [0, total) and to max_seqlen, so that malformed values give
+ * wrong results but no access outside the buffers. Rows of an empty
+ * sequence are not written. One workgroup per (sequence, head, 256-row
+ * tile of the longest sequence); causal tiles are issued last tile first, and
+ * tiles past their sequence's end exit at once. */
+FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int* cu_seqlens, int n_seq, int max_seqlen, int total,
+                         int H, int H_kv, int d, float scale, int causal, void* stream);
+
+/* Backward of fa_fwd_varlen: same packed layout and cu_seqlens contract;
+ * dout, dq: [H, total, d]; dk, dv: [H_kv, total, d] (for H_kv < H summed over
+ * each K/V head's query heads: float32 per query head in the workspace, then
+ * added in ascending head order; deterministic). One workgroup per
+ * (sequence, query head, 256-key tile of the longest sequence). dQ as in
+ * fa_bwd (float32 atomics). Rows of empty sequences get zero gradients.
+ * workspace: at least fa_bwd_varlen_workspace_bytes(total, H, H_kv, d) bytes,
+ * 256-byte aligned. */
+FA_API int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes,
+                         const int* cu_seqlens, int n_seq, int max_seqlen, int total,
+                         int H, int H_kv, int d, float scale, int causal, void* stream);
+/* fa_bwd_workspace_bytes(1, H, total, d), plus 2 x H x total x d x 4 bytes
+ * (rounded up to 256) when H_kv < H. Returns 0 for invalid sizes. */
+FA_API size_t fa_bwd_varlen_workspace_bytes(int total, int H, int H_kv, int d);
+
 /* Fixed-order (deterministic) backward, bf16 ("FlashAttention v1～v4 完整进化史",
  * v4 part 4: a deterministic backward reduces dQ across workgroups in a
  * fixed order). Same arguments, layouts, checks and mathematics as fa_bwd,

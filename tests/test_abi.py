@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -226,3 +226,41 @@ def test_gqa_workspace(lib):
     assert lib.fa_bwd_gqa_workspace_bytes(8, 32, 8, 16384, 128) == lib.fa_bwd_workspace_bytes(8, 32, 16384, 128)
     assert lib.fa_bwd_gqa_workspace_bytes(1, 6, 4, 100, 64) == 0
     assert lib.fa_bwd_gqa_workspace_bytes(1, 6, 0, 100, 64) == 0
+
+
+def test_varlen_rejects_and_workspace(lib):
+    def al(x):
+        return (x + 255) // 256 * 256
+    assert lib.fa_bwd_varlen_workspace_bytes(1000, 4, 4, 128) == lib.fa_bwd_workspace_bytes(1, 4, 1000, 128)
+    assert lib.fa_bwd_varlen_workspace_bytes(1000, 4, 2, 64) == \
+        lib.fa_bwd_workspace_bytes(1, 4, 1000, 64) + al(2 * 4 * 1000 * 64 * 4)
+    assert lib.fa_bwd_varlen_workspace_bytes(1000, 4, 3, 64) == 0
+    cu = A + 9 * GAP
+
+    def fwd(n_seq=3, max_seqlen=100, total=300, H=4, H_kv=2, d=64, **over):
+        p = dict(q=A, k=A + GAP, v=A + 2 * GAP, o=A + 3 * GAP, lse=A + 4 * GAP, cu=cu)
+        p.update(over)
+        return lib.fa_fwd_varlen(p["q"], p["k"], p["v"], p["o"], p["lse"], p["cu"], n_seq, max_seqlen, total,
+                                 H, H_kv, d, 0.125, 1, None)
+
+    def bwd(n_seq=3, max_seqlen=100, total=300, H=4, H_kv=2, d=64, ws_bytes=None, **over):
+        p = dict(cu=cu, dq=A + 6 * GAP)
+        p.update(over)
+        if ws_bytes is None:
+            ws_bytes = max(lib.fa_bwd_varlen_workspace_bytes(total, H, max(H_kv, 1), d), 1 << 20)
+        return lib.fa_bwd_varlen(A, A + GAP, A + 2 * GAP, A + 3 * GAP, A + 4 * GAP, A + 5 * GAP, p["dq"],
+                                 A + 7 * GAP, A + 8 * GAP, A + 10 * GAP, ws_bytes, p["cu"], n_seq, max_seqlen,
+                                 total, H, H_kv, d, 0.125, 1, None)
+
+    for call in (fwd, bwd):
+        assert call(n_seq=0) == _lib.FA_ERR_INVALID
+        assert call(max_seqlen=0) == _lib.FA_ERR_INVALID
+        assert call(max_seqlen=301) == _lib.FA_ERR_INVALID        # longer than the packed batch
+        assert call(H_kv=3) == _lib.FA_ERR_INVALID
+        assert call(H_kv=0) == _lib.FA_ERR_INVALID
+        assert call(d=96) == _lib.FA_ERR_UNSUPPORTED
+        assert call(cu=None) == _lib.FA_ERR_INVALID
+        assert call(cu=cu + 2) == _lib.FA_ERR_UNSUPPORTED         # misaligned
+    assert fwd(o=cu) == _lib.FA_ERR_INVALID                        # output over cu_seqlens
+    assert bwd(dq=cu) == _lib.FA_ERR_INVALID
+    assert bwd(ws_bytes=1000) == _lib.FA_ERR_INVALID
