@@ -222,6 +222,51 @@ def gqa_section(fa, steps: int, warmup: int, H_kv_list=(8, 1)):
     return {"workload": f"grouped-query causal bf16 attention, B={B} H={H} N={N} d={d}, fwd + bwd", **res}
 
 
+def varlen_section(fa, steps: int, warmup: int):
+    """Times a packed variable-length batch: 16 causal sequences with seeded
+    lengths uniform in [256, 16384] (H=32, d=128, bf16), forward + backward.
+    FLOPs are counted per sequence (4 H n^2 d / 2 forward, x2.5 backward)."""
+    import numpy as np
+    import torch
+    H, d = 32, 128
+    lens = [int(x) for x in np.random.default_rng(2400).integers(256, 16385, size=16)]
+    T = sum(lens)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(2401)
+    mk = lambda: torch.randn((H, T, d), device="cuda", generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    q, k, v, do = mk(), mk(), mk(), mk()
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), device="cuda", dtype=torch.float32)
+    g = [torch.empty_like(q) for _ in range(3)]
+    ws = torch.empty(int(fa.load().fa_bwd_varlen_workspace_bytes(T, H, H, d)), device="cuda", dtype=torch.uint8)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def run(e=None):
+        if e:
+            e[0].record()
+        fa.fwd_varlen(q, k, v, cu, max(lens), causal=True, out=o, lse=lse)
+        if e:
+            e[1].record()
+        fa.bwd_varlen(q, k, v, o, lse, do, cu, max(lens), causal=True, workspace=ws, dq=g[0], dk=g[1], dv=g[2])
+        if e:
+            e[2].record()
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    for e in ev:
+        run(e)
+    torch.cuda.synchronize()
+    f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ff = sum(attention_flops(1, H, n, d, True) for n in lens)
+    return {"workload": f"packed variable-length causal bf16 attention, 16 sequences (lengths uniform in "
+                        f"[256, 16384], seeded), total {T} rows, H={H} d={d}, fwd + bwd",
+            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+            "fwd_tflops": round(ff / (f_ms * 1e-3) / 1e12, 2), "bwd_tflops": round(2.5 * ff / (b_ms * 1e-3) / 1e12, 2),
+            "tflops": round(3.5 * ff / ((f_ms + b_ms) * 1e-3) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +277,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 workload timing")
     ap.add_argument("--no-det", action="store_true", help="skip the fixed-order backward timing")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query timing")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the variable-length batch timing")
     ap.add_argument("--fp8-only", action="store_true",
                     help="time only the fp8 workload and print its figures as one JSON line")
     ap.add_argument("--cpu-heads", type=int, default=1)
@@ -355,11 +401,15 @@ def main():
         del ws
         torch.cuda.empty_cache()
         out["bwd_det"] = det_section(fa, q, k, v, o, lse, do, True, args.steps, args.warmup, bwd_ms)
-    if not args.no_fp8 or (do_bwd and not args.no_gqa):
+    if not args.no_fp8 or (do_bwd and not (args.no_gqa and args.no_varlen)):
         del q, k, v, do, o, lse, dq, dk, dv
         torch.cuda.empty_cache()
     if do_bwd and not args.no_gqa:
         out["gqa"] = gqa_section(fa, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if do_bwd and not args.no_varlen:
+        out["varlen"] = varlen_section(fa, args.steps, args.warmup)
+        torch.cuda.empty_cache()
     if not args.no_fp8:
         torch.cuda.empty_cache()
         out["fp8"] = fp8_section(fa, args.steps, args.warmup)

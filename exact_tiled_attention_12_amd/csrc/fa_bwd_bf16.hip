@@ -140,9 +140,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   const int ts = j16 >> 2, tq = j16 & 3;     // transposed-read source row / column group
 
   int wg = blockIdx.x;
-  if (a.remap) wg = xcd_remap(wg, gridDim.x);
-  const int bhc = wg / a.n_tiles;           // (batch, K/V head, chunk), or (sequence, query head)
-  const int kt = wg - bhc * a.n_tiles;       // key tile; tile 0 (heaviest when causal) first
+  // Packed variable-length batch: key tile outermost (all sequences' and
+  // heads' tile 0 first, the heaviest of each), without the XCD grouping,
+  // which would hand some XCDs only light tiles; otherwise the tiles of one
+  // (batch, head) are grouped on one XCD, tile 0 first.
+  if (a.remap && !VARLEN) wg = xcd_remap(wg, gridDim.x);
+  const int nbh = VARLEN ? (int)gridDim.x / a.n_tiles : 0;
+  const int bhc = VARLEN ? wg % nbh : wg / a.n_tiles;       // (batch, K/V head, chunk), or (sequence, query head)
+  const int kt = VARLEN ? wg / nbh : wg - bhc * a.n_tiles;   // key tile
   // (batch, K/V head) and the chunk of its query heads. Without GQA a chunk
   // is one query head (bhc is the query head); a.group > 1 then means grouped
   // query heads handled one per workgroup.
