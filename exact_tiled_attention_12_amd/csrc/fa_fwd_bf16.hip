@@ -337,8 +337,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
         fetch(i + AHEAD - NM, nxt, nkt, nvt);
       // This step's share of the ring loads, one load per few products.
       if constexpr (LP >= 0) {
-        if (i == 2) issue_load(ld_tile, ld_stage, LP, false);
-        if (i == NM / 2 + 2) issue_load(ld_tile, ld_stage, LP, true);
+        if (i == 1) issue_load(ld_tile, ld_stage, LP, false);
+        if (i == 3) issue_load(ld_tile, ld_stage, LP, true);
       }
       const int k = pos_idx(i);
       if (pos_is_s(i)) {
