@@ -141,13 +141,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
   int wg = blockIdx.x;
   // Packed variable-length batch: key tile outermost (all sequences' and
-  // heads' tile 0 first, the heaviest of each), without the XCD grouping,
-  // which would hand some XCDs only light tiles; otherwise the tiles of one
-  // (batch, head) are grouped on one XCD, tile 0 first.
+  // heads' tile 0 first, the heaviest of each); with the (sequence, head)
+  // pairs a multiple of 8, each pair stays on one XCD (workgroups go to XCDs
+  // round-robin by id) and every XCD runs its pairs tile-major. Otherwise the
+  // tiles of one (batch, head) are grouped on one XCD, tile 0 first.
   if (a.remap && !VARLEN) wg = xcd_remap(wg, gridDim.x);
   const int nbh = VARLEN ? (int)gridDim.x / a.n_tiles : 0;
-  const int bhc = VARLEN ? wg % nbh : wg / a.n_tiles;       // (batch, K/V head, chunk), or (sequence, query head)
-  const int kt = VARLEN ? wg / nbh : wg - bhc * a.n_tiles;   // key tile
+  int bhc_, kt_;
+  if (VARLEN && a.remap && (nbh & 7) == 0) {
+    const int x = wg & 7, j = wg >> 3, per = nbh >> 3;
+    kt_ = j / per;
+    bhc_ = (j - kt_ * per) * 8 + x;
+  } else {
+    bhc_ = VARLEN ? wg % nbh : wg / a.n_tiles;
+    kt_ = VARLEN ? wg / nbh : wg - bhc_ * a.n_tiles;
+  }
+  const int bhc = bhc_;       // (batch, K/V head, chunk), or (sequence, query head)
+  const int kt = kt_;         // key tile
   // (batch, K/V head) and the chunk of its query heads. Without GQA a chunk
   // is one query head (bhc is the query head); a.group > 1 then means grouped
   // query heads handled one per workgroup.

@@ -141,9 +141,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   int wg = blockIdx.x;
-  if (a.remap) wg = xcd_remap(wg, gridDim.x);
-  const int bh = wg / a.n_qtiles;   // (batch, head), or (sequence, head) for VARLEN
-  const int t = wg - bh * a.n_qtiles;
+  int bh, t;
+  // Packed variable-length batch (with the pairs a multiple of 8): each
+  // (sequence, head) stays on one XCD (workgroups go to XCDs round-robin by
+  // id), and every XCD runs its pairs' tiles tile-major, the heaviest causal
+  // tiles (last of the longest sequences) first. Otherwise the tiles of one
+  // (batch, head) are grouped on one XCD, heaviest first.
+  const int nsh = gridDim.x / a.n_qtiles;        // (sequence, head) pairs
+  if (VARLEN && a.remap && (nsh & 7) == 0) {
+    const int x = wg & 7, j = wg >> 3;           // XCD, position within it
+    const int per = nsh >> 3;
+    t = j / per;
+    bh = (j - t * per) * 8 + x;
+  } else {
+    if (a.remap) wg = xcd_remap(wg, gridDim.x);
+    bh = wg / a.n_qtiles;   // (batch, head), or (sequence, head) for VARLEN
+    t = wg - bh * a.n_qtiles;
+  }
   const int qt = CAUSAL ? (a.n_qtiles - 1 - t) : t;
   int N = a.N;
   size_t base, kv_base, lse_base;
