@@ -117,12 +117,6 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   if (rc) return rc;
   rc = check_kv_heads(H, H_kv);
   if (rc) return rc;
-  // A workgroup addresses the dQ accumulator rows of all the query heads it
-  // visits with 32-bit byte offsets.
-  const int chunks = H_kv < H ? fa::bwd_gqa_chunks(B, H, H_kv, N) : 1;
-  if ((long long)(H / H_kv / chunks) * N * d * 4 >= (1LL << 31))
-    return fail(FA_ERR_UNSUPPORTED, "group too large: %d query heads x N = %d x d = %d float32 reach 2^31 bytes",
-                H / H_kv / chunks, N, d);
   if (det && (size_t)fa::bwd_row_tiles(N) * fa::kBwdPartFloats * 4 > (1u << 31))
     return fail(FA_ERR_UNSUPPORTED, "sequence too long for the fixed-order backward (N = %d)", N);
   const size_t need = det ? fa_bwd_det_workspace_bytes(B, H, N, d, causal)
@@ -144,7 +138,7 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.N = N; a.scale = scale; a.c = log2e_scale(scale);
-  a.H = H; a.group = H / H_kv; a.hchunks = chunks; a.B = B;
+  a.H = H; a.group = H / H_kv; a.B = B;
   if (det) {
     // D first, then the partial tiles.
     a.dvec = (float*)ws;
@@ -152,8 +146,8 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   } else {
     a.dq_acc = (float*)ws;
     a.dvec = (float*)((char*)ws + align256((size_t)B * H * N * d * 4));
-    // grouped-query with several head chunks: float32 dK, dV per chunk after D
-    if (chunks > 1) a.dkv_part = (float*)((char*)ws + fa_bwd_workspace_bytes(B, H, N, d));
+    // grouped K/V heads: float32 dK, dV per query head after D
+    if (H_kv < H) a.dkv_part = (float*)((char*)ws + fa_bwd_workspace_bytes(B, H, N, d));
   }
   return launched(fa::launch_bwd(dt, d, causal, a, B, H, stage_mask, (hipStream_t)stream), "attention backward");
 }
@@ -221,9 +215,8 @@ int fa_bwd_det(const void* q, const void* k, const void* v, const void* o, const
 size_t fa_bwd_gqa_workspace_bytes(int B, int H, int H_kv, int N, int d) {
   const size_t base = fa_bwd_workspace_bytes(B, H, N, d);
   if (base == 0 || H_kv < 1 || H_kv > H || H % H_kv != 0) return 0;
-  const int chunks = H_kv < H ? fa::bwd_gqa_chunks(B, H, H_kv, N) : 1;
-  if (chunks == 1) return base;
-  return base + align256((size_t)2 * B * H_kv * chunks * N * d * 4);
+  // grouped K/V heads: float32 dK and dV per query head, [B H_kv][G][N][d] each
+  return H_kv < H ? base + align256((size_t)2 * B * H * N * d * 4) : base;
 }
 
 int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
@@ -302,7 +295,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.N = total; a.scale = scale; a.c = log2e_scale(scale);
-  a.H = H; a.group = H / H_kv; a.hchunks = H / H_kv; a.B = 1;
+  a.H = H; a.group = H / H_kv; a.B = 1;
   a.cu_seqlens = cu_seqlens; a.n_seq = n_seq; a.max_seqlen = max_seqlen;
   a.dq_acc = (float*)workspace;
   a.dvec = (float*)((char*)workspace + align256((size_t)H * total * d * 4));

@@ -167,8 +167,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_det_kernel(BwdArgs a, long lo
 }
 
 // ------------------------------------- grouped-query dK, dV chunk sum
-// dk, dv [B, H_kv, N, d] = sum over the head chunks c = 0, 1, ... (in that
-// order) of the chunks' float32 dK (already scaled) and dV, rounded to bf16.
+// dk, dv [B, H_kv, N, d] = sum over the group's query heads c = 0, 1, ... (in
+// that order) of their float32 dK (already scaled) and dV, rounded to bf16.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dkv_sum_kernel(BwdArgs a, long long n4) {
   const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_sum_kernel(BwdArgs a, long l
   const long long e = 4 * i;                          // element of [B H_kv][N][d]
   const long long per_head = (long long)a.N * D;
   const long long bh = e / per_head, in_head = e - bh * per_head;
-  const int C = a.hchunks;
+  const int C = a.group;
   const float* pk = a.dkv_part + (size_t)bh * C * per_head + in_head;
   const float* pv = pk + (size_t)n4 * 4 * C;
   f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
@@ -467,7 +467,7 @@ hipError_t run(int causal, BwdArgs a, int B, int H, int stage_mask, hipStream_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (sizeof(typename Tr::T) == 2) {
-      if (a.dkv_part != nullptr) {   // grouped-query with several head chunks
+      if (a.dkv_part != nullptr) {   // grouped K/V heads
         const long long m4 = (long long)B * (H / a.group) * a.N * D / 4;
         const int mb = (int)((m4 + kThreads - 1) / kThreads);
         hipLaunchKernelGGL((bwd_dkv_sum_kernel<D>), dim3(mb), dim3(kThreads), 0, s, a, m4);

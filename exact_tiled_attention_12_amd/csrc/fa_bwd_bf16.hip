@@ -112,16 +112,13 @@ __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // DET: dQ contributions go to partial tiles (plain stores, one tile per
 // visited (key tile, query tile) pair) instead of float32 atomics.
-// GQA: the key tile belongs to a K/V head shared by a.group consecutive query
-// heads, split into a.hchunks chunks; the workgroup of a chunk of several heads
-// visits the query tiles of each of them in turn, so dK and dV sum over the
-// chunk in registers. (Chunks of one head run the GQA = false kernel.) With
-// more than one chunk, each chunk's float32 dK and dV go to the workspace
-// for a fixed-order sum over chunks.
+// Grouped K/V heads (a.group > 1): one query head per workgroup with its
+// group's K/V head; float32 dK and dV of each query head go to the workspace
+// for a fixed-order sum over the group.
 // VARLEN: packed variable-length batch, one workgroup per (sequence, query
 // head, key tile) with the sequence's rows and length; key tiles past the
 // sequence's end exit at once.
-template <int D, bool CAUSAL, bool DET, bool GQA, bool VARLEN = false>
+template <int D, bool CAUSAL, bool DET, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // Device pass only (the host pass needs just the launch stub).
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -158,12 +155,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   }
   const int bhc = bhc_;       // (batch, K/V head, chunk), or (sequence, query head)
   const int kt = kt_;         // key tile
-  // (batch, K/V head) and the chunk of its query heads. Without GQA a chunk
-  // is one query head (bhc is the query head); a.group > 1 then means grouped
-  // query heads handled one per workgroup.
+  // (batch or sequence, K/V head) and the query head's index in its group.
   int N, bh, chunk;
   size_t base, qbase, lbase, pbase;   // K/V rows, query rows, L/D rows, float32 dK/dV partial rows
-  const int G = GQA ? a.group / a.hchunks : 1;         // query heads this workgroup visits
   if constexpr (VARLEN) {
     // Rows cu[seq] .. cu[seq+1]-1 of every head (T = a.N rows per head);
     // clamped to the packed tensor and to max_seqlen, so that malformed
@@ -184,15 +178,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     pbase = (((size_t)bh * a.group + chunk) * T + s0) * D;
   } else {
     N = a.N;
-    bh = GQA ? bhc / a.hchunks : (a.group == 1 ? bhc : bhc / a.group);
-    chunk = bhc - bh * (GQA ? a.hchunks : a.group);
-    // First query head of the chunk (the query heads of K/V head j of batch b
-    // are b H + j group .. b H + j group + group - 1).
-    const int qh0 = GQA ? (bh / (a.H / a.group)) * a.H + (bh % (a.H / a.group)) * a.group + chunk * G : bhc;
+    // bhc is the query head (b H + h); its K/V head is bhc / group.
+    bh = a.group == 1 ? bhc : bhc / a.group;
+    chunk = bhc - bh * a.group;
+    const int qh0 = bhc;
     base = (size_t)bh * (size_t)N * D;
     qbase = (size_t)qh0 * (size_t)N * D;
     lbase = (size_t)qh0 * N;
-    pbase = ((size_t)bh * a.hchunks + chunk) * (size_t)N * D;
+    pbase = ((size_t)bh * a.group + chunk) * (size_t)N * D;
   }
   const unsigned head_bytes = (unsigned)N * C::RB;
   // Query-side buffers start at the group's first head; a visit to head g of
@@ -214,18 +207,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   const int n_qt = (N + kBR - 1) / kBR;
   const int qt_begin = CAUSAL ? k0 / kBR : 0;
   const int nt = n_qt - qt_begin;   // query tiles visited per query head (>= 1)
-  const int nvis = G * nt;          // visits: head 0's tiles, then head 1's, ...
-  // Visit i: query head g = i / nt of the chunk, tile n_qt - 1 - (i % nt).
-  // (GQA: the loop forms i / nt once per visit and passes the quotients of
-  // visits i - 1 and i + 2 on, so vhead / vtile take it as an argument.)
-  auto vhead = [&](int i, int q) INL { return GQA ? q : 0; };
-  auto vtile = [&](int i, int q) INL { return n_qt - 1 - (GQA ? i - q * nt : i); };
+  const int nvis = nt;              // visits: query tile n_qt - 1 - i at visit i
   const __amdgpu_buffer_rsrc_t rdq =
       DET ? make_rsrc(a.dq_part + ((size_t)bh * (size_t)bwd_det_parts(N, CAUSAL) +
                                    (size_t)bwd_part_offset(N, CAUSAL, kt)) * kBwdPartFloats +
                           (size_t)(D == 64 ? (wave >> 1) : 0) * nt * kBR * D - (size_t)qt_begin * kBR * D,
                       (unsigned)n_qt * kBR * D * 4)
-          : make_rsrc(a.dq_acc + qbase, (unsigned)G * N * D * 4);
+          : make_rsrc(a.dq_acc + qbase, (unsigned)N * D * 4);
   const unsigned kt_a = (unsigned)(uintptr_t)LDS(unsigned char, kt_s);
   const unsigned rg_a = (unsigned)(uintptr_t)LDS(unsigned char, rg_s);
 
@@ -240,30 +228,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // copy of L (even waves) or D (odd waves) of the tile's 32 rows; lanes 8..63
   // of that copy read past the row range and write zeros behind it. Two
   // waves copy the same L or D bytes to the same place.
-  auto issue_qtile = [&](int i, int iq) INL {
+  auto issue_qtile = [&](int i) INL {
+    const int qt = n_qt - 1 - i;
     const bool live = i < nvis;
-    const int hg = live ? vhead(i, iq) : 0;
-    const int qt = live ? vtile(i, iq) : 0;
-    const int r0 = hg * N + qt * kBR;   // first row, counted from the group's first head
-    i32x4 q_r = rq, g_r = rg, l_r = rl, d_r = rd;
-    if constexpr (GQA) {
-      q_r[2] = g_r[2] = __builtin_amdgcn_readfirstlane((hg + 1) * (int)head_bytes);
-      l_r[2] = d_r[2] = __builtin_amdgcn_readfirstlane((hg + 1) * N * 4);
-    }
     const unsigned so = rg_a + (i % kStages) * C::STAGE;
 #pragma unroll
     for (int u = 0; u < C::QT_LOADS; ++u) {
       const int t = wave * C::QT_LOADS + u;
-      copy_rows(q_r, so, r0, t, live);
-      copy_rows(g_r, so + C::QT, r0, t, live);
+      copy_rows(rq, so, qt * kBR, t, live);
+      copy_rows(rg, so + C::QT, qt * kBR, t, live);
     }
-    const unsigned lo = (unsigned)r0 * 4 + 16 * lane;
+    const unsigned lo = (unsigned)(qt * kBR) * 4 + 16 * lane;
     const unsigned off = live && lane < 8 ? lo : 0x80000000u;
     if (wave & 1)
-      dma_load16(d_r, so + 2 * C::QT + C::LD, off);
+      dma_load16(rd, so + 2 * C::QT + C::LD, off);
     else
-      dma_load16(l_r, so + 2 * C::QT, off);
+      dma_load16(rl, so + 2 * C::QT, off);
   };
+
 
   // K tile (whole workgroup), V operands, then the first two query tiles.
 #pragma unroll
@@ -277,8 +259,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       const unsigned off = (unsigned)(kw0 + kb * 32 + l32) * C::RB + kk * 32 + hh * 16;
       vf[kb][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
-  issue_qtile(0, 0);
-  issue_qtile(1, GQA ? (nt == 1 ? 1 : 0) : 0);
+  issue_qtile(0);
+  issue_qtile(1);
 
   // ---- per-lane LDS addresses (byte offsets; chunk bits XORed per step).
   // Rows of a 32-row block read with lanes = one row each (Q, dO: permuted).
@@ -333,9 +315,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // `visit`, at the rows' own offsets in rdq. A tile that does not exist (or
   // rows past N) gets offsets past the buffer: the operations are no-ops, so
   // the number of memory operations per tile is the same everywhere.
-  auto dq_atomic = [&](const f32x16& acc, int visit, int vq, bool live, int r) INL {
-    const int q = vtile(visit, vq) * kBR + 8 * (r >> 2) + 4 * hh + (r & 3);
-    const unsigned off = live && q < N ? ((unsigned)(vhead(visit, vq) * N + q) * D + db_q * 32 + l32) * 4 : 0x80000000u;
+  auto dq_atomic = [&](const f32x16& acc, int visit, bool live, int r) INL {
+    const int q = (n_qt - 1 - visit) * kBR + 8 * (r >> 2) + 4 * hh + (r & 3);
+    const unsigned off = live && q < N ? ((unsigned)q * D + db_q * 32 + l32) * 4 : 0x80000000u;
     if constexpr (DET) {
       // (Bit cast of a copy: hipcc compiled a bit cast applied directly to an
       // element of a vector variable as a cast of its first element.)
@@ -346,9 +328,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     }
   };
   constexpr int NDQ = 16;   // dQ memory operations per visit
-  auto dq_atomics = [&](const f32x16& acc, int visit, int vq, bool live) INL {
+  auto dq_atomics = [&](const f32x16& acc, int visit, bool live) INL {
 #pragma unroll
-    for (int r = 0; r < NDQ; ++r) dq_atomic(acc, visit, vq, live, r);
+    for (int r = 0; r < NDQ; ++r) dq_atomic(acc, visit, live, r);
   };
 
   __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS));   // K tile, V operands, query tile 0
@@ -361,11 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   // i % 3; its dS^T goes to dS buffer i % 2, which dQ of visit i reads during
   // visit i + 1.
   for (int i = 0; i < nvis; ++i) {
-    // head (quotient by nt) of visits i, i - 1 and i + 2
-    const int iq = GQA ? i / nt : 0;
-    const int iq_prev = GQA ? (i - iq * nt == 0 ? iq - 1 : iq) : 0;
-    const int iq_next = GQA ? (i + 2 - iq * nt >= 2 * nt ? iq + 2 : i + 2 - iq * nt >= nt ? iq + 1 : iq) : 0;
-    const int qt = vtile(i, iq);
+    const int qt = n_qt - 1 - i;
     if (i > 0) {
       // Memory operations issued after visit i's own copies: (i >= 2) the NDQ
       // dQ operations of visit i-2, then the copies of visit i+1 and the NDQ
@@ -441,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       // Copies of visit i+2 go to the stage of visit i-1 (free since the
       // barrier). Issued here rather than right after the barrier, where
       // they would queue behind the previous visit's dQ atomics and stall.
-      if (kb == 1) issue_qtile(i + 2, iq_next);
+      if (kb == 1) issue_qtile(i + 2);
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
       if (kb == 1) ldv[0] = rd_ld(0);
@@ -536,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
         constexpr int NA = NS - QS;
         const int lo = (step - QS) * NDQ / NA, hi = (step - QS + 1) * NDQ / NA;
 #pragma unroll
-        for (int r = lo; r < hi; ++r) dq_atomic(dq_acc, i - 1, iq_prev, i > 0, r);
+        for (int r = lo; r < hi; ++r) dq_atomic(dq_acc, i - 1, i > 0, r);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -557,7 +535,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       dq_acc = mma(join(qop[m % 3].v[0], qop[m % 3].v[1]), join(qop[m % 3].v[2], qop[m % 3].v[3]), dq_acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    dq_atomics(dq_acc, nvis - 1, G - 1, true);
+    dq_atomics(dq_acc, nvis - 1, true);
   }
 
   // Epilogue: dK = scale * acc, dV = acc (lanes = d, rows = keys); rows past N dropped.
@@ -565,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     // float32 dK and dV of this chunk: [batch, K/V head][chunk][N][d] each
     // (VARLEN: [K/V head][chunk][T][d], this sequence's rows).
     const size_t pb = pbase;
-    const size_t half = (size_t)(a.H / a.group) * a.hchunks * (size_t)a.N * D * (size_t)(a.B);
+    const size_t half = (size_t)a.H * (size_t)a.N * D * (size_t)(a.B);
     const __amdgpu_buffer_rsrc_t rpk = make_rsrc(a.dkv_part + pb, (unsigned)N * D * 4);
     const __amdgpu_buffer_rsrc_t rpv = make_rsrc(a.dkv_part + half + pb, (unsigned)N * D * 4);
 #pragma unroll
@@ -607,25 +585,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
 template <int D, bool CAUSAL, bool DET>
 void launch_main(const BwdArgs& a, long long grid, hipStream_t s) {
-  if (a.cu_seqlens != nullptr)   // packed variable-length batch, one query head per workgroup
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, false, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
-  else if constexpr (DET)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
-  else if (a.group > a.hchunks)   // several query heads per workgroup
+  if (a.cu_seqlens != nullptr)   // packed variable-length batch
     hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, false, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, DET, false>), dim3(grid), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16_main(int d, int causal, BwdArgs a, int B, int H, hipStream_t s) {
-  // One workgroup per (batch, K/V head, head chunk, key tile), or, for a
-  // packed variable-length batch, per (sequence, query head, key tile of the
+  // One workgroup per (batch, query head, key tile), or, for a packed
+  // variable-length batch, per (sequence, query head, key tile of the
   // longest sequence).
   a.n_tiles = ((a.cu_seqlens != nullptr ? a.max_seqlen : a.N) + kBC - 1) / kBC;
   const long long grid = a.cu_seqlens != nullptr ? (long long)a.n_seq * H * a.n_tiles
-                                                 : (long long)B * (H / a.group) * a.hchunks * a.n_tiles;
+                                                 : (long long)B * H * a.n_tiles;
   a.remap = grid % 8 == 0 ? 1 : 0;
   const bool det = a.dq_part != nullptr;
   if (d == 64) {

@@ -47,9 +47,8 @@ struct BwdArgs {
   int remap;      // filled by the launcher
   int H;          // query heads
   int group;      // query heads per K/V head (1 unless grouped-query, bf16 only)
-  int hchunks;    // grouped-query: workgroups (head chunks) per K/V head and key tile
   int B;          // batch
-  float* dkv_part;  // grouped-query with hchunks > 1: float32 dK, dV per chunk, else nullptr
+  float* dkv_part;  // grouped K/V heads: float32 dK, dV per query head, [B H_kv][group][N][d] each; else nullptr
   // Packed variable-length batch: cumulative sequence lengths [B + 1], or
   // nullptr. N is then the packed length T (the row stride of a head; B = 1
   // for the streaming passes) and max_seqlen bounds every sequence.
@@ -57,18 +56,6 @@ struct BwdArgs {
   int n_seq;
   int max_seqlen;
 };
-
-// Grouped-query backward: chunks of each K/V head's query heads, one
-// workgroup per (batch, K/V head, chunk, 256-key tile). The smallest divisor
-// of the group size that gives at least 2048 workgroups (all of them: one
-// head per chunk, if none does). Depends on the sizes only.
-inline int bwd_gqa_chunks(int B, int H, int H_kv, int N) {
-  const int G = H / H_kv;
-  const long long base = (long long)B * H_kv * ((N + 255) / 256);
-  for (int c = 1; c < G; ++c)
-    if (G % c == 0 && base * c >= 2048) return c;
-  return G;
-}
 
 struct QuantArgs {
   const void* x;       // bf16 [B,H,N,d]

@@ -116,15 +116,13 @@ FA_API int fa_bwd_stages(const void* q, const void* k, const void* v, const void
  * multiple of H_kv; lse: [B,H,N]. The H query heads form H_kv groups of
  * G = H / H_kv consecutive heads, and query head h attends with K/V head
  * h / G (MQA: H_kv = 1; H_kv = H is fa_fwd / fa_bwd). dk and dv of a K/V
- * head are the sums over the G query heads that read it: the backward splits
- * each group into chunks of consecutive heads (a function of B, H, H_kv and
- * N only), sums a chunk in the accumulators of one workgroup, and, with
- * more than one chunk, adds the chunks' float32 sums in ascending chunk order
- * in a final pass; dk and dv are deterministic. The backward's workspace is
- * fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, d), and a chunk's heads x N x d x
- * 4 bytes must be below 2^31. Same conventions, checks and rounding as
- * fa_fwd / fa_bwd; H_kv out of range or not dividing H gives
- * FA_ERR_INVALID. */
+ * head are the sums over the G query heads that read it: the backward runs
+ * one workgroup per (batch, query head, 256-key tile) with the group's K/V
+ * head, writes each query head's float32 dK and dV to the workspace, and a
+ * final pass adds them in ascending head order; dk and dv are deterministic.
+ * The backward's workspace is fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, d).
+ * Same conventions, checks and rounding as fa_fwd / fa_bwd; H_kv out of
+ * range or not dividing H gives FA_ERR_INVALID. */
 FA_API int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int H_kv, int N, int d, float scale, int causal, void* stream);
 FA_API int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -132,8 +130,8 @@ FA_API int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes,
                       int B, int H, int H_kv, int N, int d, float scale, int causal, void* stream);
 /* Bytes of device workspace fa_bwd_gqa needs: fa_bwd_workspace_bytes(B, H,
- * N, d) plus, when a group is split into several chunks, float32 dK and dV
- * per chunk (2 x B x H_kv x chunks x N x d x 4 bytes, rounded up to 256).
+ * N, d) plus, when H_kv < H, float32 dK and dV per query head (2 x B x H x
+ * N x d x 4 bytes, rounded up to 256).
  * Returns 0 for invalid sizes. */
 FA_API size_t fa_bwd_gqa_workspace_bytes(int B, int H, int H_kv, int N, int d);
 

@@ -125,19 +125,15 @@ def test_gqa_long_context_sampled_heads(fa):
     _check_grads([dq[:, grp], dk[:, j:j + 1], dv[:, j:j + 1]], ref, "gqa H=32/4 N=4096 group 1")
 
 
-@pytest.mark.parametrize("B,H,H_kv,N,d,chunks", [
-    (64, 4, 2, 4096, 64, 1),    # 2048 workgroups unsplit: each sums its 2 heads in registers
-    (64, 8, 1, 2048, 128, 4),   # 4 chunks of 2 heads: registers, then the fixed-order chunk sum
-])
-def test_gqa_head_chunks(fa, B, H, H_kv, N, d, chunks):
-    """Groups summed in one workgroup, and groups split into multi-head
-    chunks: sampled batches against the oracle, dK/dV bits repeatable."""
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(64, 4, 2, 4096, 64), (64, 8, 1, 2048, 128)])
+def test_gqa_large_batches(fa, B, H, H_kv, N, d):
+    """Many batches: sampled (batch, K/V head) pairs against the oracle, and
+    dK/dV bits repeatable (per-head float32 sums added in a fixed order)."""
     import torch
-    base = fa.bwd_workspace_bytes(B, H, N, d)
-    extra = 2 * B * H_kv * chunks * N * d * 4 if chunks > 1 else 0
-    assert fa.bwd_gqa_workspace_bytes(B, H, H_kv, N, d) == base + extra   # the split under test
+    assert fa.bwd_gqa_workspace_bytes(B, H, H_kv, N, d) == \
+        fa.bwd_workspace_bytes(B, H, N, d) + 2 * B * H * N * d * 4
     w, x, (q, k, v, do) = _inputs(1900 + H, B, H, H_kv, N, d, True)
-    announce(f"fa_bwd_gqa chunks={chunks} B={B} H={H} H_kv={H_kv} N={N} d={d}")
+    announce(f"fa_bwd_gqa B={B} H={H} H_kv={H_kv} N={N} d={d}")
     o, lse = fa.fwd(q, k, v, causal=True)
     g1 = fa.bwd(q, k, v, o, lse, do, causal=True)
     g2 = fa.bwd(q, k, v, o, lse, do, causal=True)
@@ -151,4 +147,4 @@ def test_gqa_head_chunks(fa, B, H, H_kv, N, d, chunks):
         ref = A.backward_gqa(x["q"][b:b + 1, grp], x["k"][b:b + 1, j:j + 1], x["v"][b:b + 1, j:j + 1],
                              x["do"][b:b + 1, grp], w.scale, True)
         _check_grads([dq[b:b + 1, grp], dk[b:b + 1, j:j + 1], dv[b:b + 1, j:j + 1]], ref,
-                     f"gqa chunks={chunks} batch {b} K/V head {j}")
+                     f"gqa batch {b} K/V head {j}")
