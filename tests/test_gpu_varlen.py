@@ -52,6 +52,8 @@ LENGTH_MIXES = {
     "ragged": [300, 1, 0, 517, 64, 255, 257],
     "one long": [1200, 3, 40],
     "equal": [256, 256, 256],
+    "single": [777],
+    "mostly empty": [0, 0, 5, 0, 1, 0],
 }
 
 
