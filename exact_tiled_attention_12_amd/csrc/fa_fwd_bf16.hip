@@ -142,13 +142,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   int wg = blockIdx.x;
   int bh, t;
-  // With the (batch or sequence, head) pairs a multiple of 8, each pair stays
-  // on one XCD (workgroups go to XCDs round-robin by id) and every XCD runs
-  // its pairs' tiles tile-major, the heaviest causal tiles (the last ones, of
-  // the longest sequences) first. Otherwise the tiles of one pair are grouped
-  // on one XCD, heaviest first.
+  // Causal or packed variable-length, with the (batch or sequence, head)
+  // pairs a multiple of 8: each pair stays on one XCD (workgroups go to XCDs
+  // round-robin by id) and every XCD runs its pairs' tiles tile-major, the
+  // heaviest tiles (the last ones, of the longest sequences) first.
+  // Otherwise the tiles of one pair are grouped on one XCD and run in order
+  // (causal: heaviest first); with equal tiles that keeps a head's K/V in L2.
   const int nsh = gridDim.x / a.n_qtiles;        // (batch or sequence, head) pairs
-  if (a.remap && (nsh & 7) == 0) {
+  if ((CAUSAL || VARLEN) && a.remap && (nsh & 7) == 0) {
     const int x = wg & 7, j = wg >> 3;           // XCD, position within it
     const int per = nsh >> 3;
     t = j / per;
