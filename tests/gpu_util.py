@@ -79,3 +79,47 @@ def grad_rounding_bound(q, k, v, o, lse, do, scale: float, causal: bool):
     ds = np.abs(p * (do @ v.T - np.sum(do * o, axis=1)[:, None]))
     u = 2.0 ** -8
     return u * scale * (ds @ np.abs(k)), u * scale * (ds.T @ np.abs(q)), u * (np.abs(p).T @ np.abs(do))
+
+
+def saved_inputs_bound(q, k, v, do, scale: float, causal: bool, tol_o: float, tol_l: float):
+    """Per-element bound on the backward from a forward's saved O and L, for one head.
+
+    All inputs are the oracle's: q, k, v, do as the GPU sees them, O and L
+    recomputed here from the plain definition. The backward takes the saved O
+    and L of a forward whose O is within tol_o and whose L is within tol_l of
+    the exact values (each asserted by the caller before this bound is used).
+    With the exact P, dS and D of the oracle:
+      * an error |dL| <= tol_l in L changes P = exp(S - L) by a factor
+        exp(-dL), so |P' - P| <= r P with r = expm1(tol_l);
+      * an error of at most tol_o in each element of O moves
+        D_i = rowsum(dO_i * O_i) by at most dD_i = tol_o * sum_k |dO_ik|;
+      * dS' - dS = P rho (dP - D) - P (1 + rho) dD, so
+        |dS' - dS| <= E = r |dS| + (1 + r) P dD and |dS'| <= |dS| + E;
+      * dQ = scale dS K, dK = scale dS^T Q and dV = P^T dO are linear in dS
+        and P, so the propagated error is scale E |K|, scale E^T |Q| and
+        r P^T |dO|;
+      * the kernel's own bf16 rounding of P' and dS' adds the bound of
+        grad_rounding_bound taken on |P'| <= (1 + r) P and |dS'| <= |dS| + E.
+    Returns (bq, bk, bv) shaped like dQ, dK, dV.
+    """
+    q, k, v, do = (np.asarray(a, np.float64) for a in (q, k, v, do))
+    n = q.shape[0]
+    s = scale * (q @ k.T)
+    if causal:
+        s = np.where(np.tril(np.ones((n, n), bool)), s, -np.inf)
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = e / np.sum(e, axis=1, keepdims=True)
+    o = p @ v
+    ds = np.abs(p * (do @ v.T - np.sum(do * o, axis=1)[:, None]))
+    r = float(np.expm1(tol_l))
+    dd = tol_o * np.sum(np.abs(do), axis=1)
+    err = r * ds + (1.0 + r) * p * dd[:, None]
+    ds_max = ds + err
+    p_max = (1.0 + r) * p
+    u = 2.0 ** -8
+    ak, aq, ado = np.abs(k), np.abs(q), np.abs(do)
+    bq = scale * (err @ ak) + u * scale * (ds_max @ ak)
+    bk = scale * (err.T @ aq) + u * scale * (ds_max.T @ aq)
+    bv = r * (p.T @ ado) + u * (p_max.T @ ado)
+    return bq, bk, bv

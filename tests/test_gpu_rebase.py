@@ -10,16 +10,23 @@ maximum in the first block, so these cases make it move later:
   * shrinking keys: the first block holds the maximum (no re-base after it).
 Forward results are compared with the float64 oracle at the stated bf16
 tolerances (O 2e-2, LSE 1e-3). The backward, which recomputes P from the
-saved LSE, is compared with the oracle's backward step on the same saved O
-and LSE; the bound is the bf16 gradient bound of the backward tests plus the
-propagated bf16 rounding of P and dS (large keys make dS K cancel).
+saved LSE, is checked two ways, with references and bounds computed from the
+oracle only:
+  * the step alone, fed the oracle's O (rounded to bf16) and L, against the
+    exact backward step on those inputs; the bound is the bf16 gradient bound
+    of the backward tests plus the propagated bf16 rounding of P and dS
+    (large keys make dS K cancel);
+  * end to end from the original inputs (GPU forward, then GPU backward)
+    against the oracle's exact gradients, after the forward's O and L have
+    been checked at the stated tolerances; the bound adds what those
+    tolerances can move through D = rowsum(dO * O) and P = exp(S - L).
 """
 
 import numpy as np
 import pytest
 
 import seeded_inputs as si
-from gpu_util import announce, bf16_from_f32, bf16_ulp, grad_rounding_bound, host, max_abs
+from gpu_util import announce, bf16_from_f32, bf16_ulp, grad_rounding_bound, host, max_abs, saved_inputs_bound
 from oracle import attention as A
 
 pytestmark = pytest.mark.gpu
@@ -74,8 +81,69 @@ def test_forward_against_oracle(fa, kind, N, d, causal):
     assert el <= 1e-3, f"LSE max-abs {el:.3e}"
 
 
-@pytest.mark.parametrize("kind,N,d,causal", [c for c in CASES if c[1] == 700])
-def test_backward_against_oracle(fa, kind, N, d, causal):
+BWD_CASES = [c for c in CASES if c[1] == 700]
+
+# Stated tolerances of the bf16 forward (O max-abs, LSE max-abs).
+TOL_O, TOL_L = 2e-2, 1e-3
+
+
+def _head_bounds(fn, vals, H, head_args):
+    """Per-head bounds of a helper, stacked into [1, H, ...] arrays;
+    head_args(h) gives the helper's arguments after q, k, v of head h."""
+    out = None
+    for h in range(H):
+        b = fn(vals["q"][0, h], vals["k"][0, h], vals["v"][0, h], *head_args(h))
+        if out is None:
+            out = [np.empty((1, H) + x.shape) for x in b]
+        for t, x in zip(out, b):
+            t[0, h] = x
+    return out
+
+
+def _check_grads(grads, ref, extra, label):
+    for name, g, r, ex in zip(("dQ", "dK", "dV"), grads, ref, extra):
+        g = host(g)
+        assert np.all(np.isfinite(g)), f"{name} not finite"
+        bound = np.maximum(2e-2, bf16_ulp(r)) + ex
+        err = max_abs(g, r)
+        print(f"{label} {name}: max-abs {err:.2e} (max|ref| {np.max(np.abs(r)):.3g}, "
+              f"worst err/bound {np.max(np.abs(g - r) / bound):.3f})")
+        assert bool(np.all(np.abs(g - r) <= bound)), f"{name} max-abs {err:.3e}"
+
+
+@pytest.mark.parametrize("kind,N,d,causal", BWD_CASES)
+def test_backward_step_on_oracle_saved(fa, kind, N, d, causal):
+    """The backward step alone, fed the oracle's saved O (rounded to bf16, the
+    forward's output type) and L (float32) instead of a GPU forward's: the
+    reference is the exact backward step on those same inputs
+    ("6.1 FlashAttention V1详解", sections 6.1-6.2), and the bound adds only
+    the kernel's own bf16 rounding of P and dS, taken on oracle values."""
+    import torch
+    dev, vals = _inputs(kind, 1, 2, N, d, 1300 + N + d)
+    scale = 1.0 / np.sqrt(d)
+    o_ref, l_ref = A.forward(vals["q"], vals["k"], vals["v"], scale, causal)
+    o_bits, o_b = si.bf16_round(o_ref.astype(np.float32))
+    l_f = l_ref.astype(np.float32)
+    o_dev = torch.from_numpy(o_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    l_dev = torch.from_numpy(l_f).cuda()
+    announce(f"fa_bwd rebase step {kind} N={N} d={d} causal={causal}")
+    grads = fa.bwd(dev["q"], dev["k"], dev["v"], o_dev, l_dev, dev["do"], causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = A.backward_from_saved(vals["q"], vals["k"], vals["v"], o_b, l_f.astype(np.float64), vals["do"],
+                                scale, causal)
+    extra = _head_bounds(grad_rounding_bound, vals, 2,
+                         lambda h: (o_b[0, h], l_f[0, h].astype(np.float64), vals["do"][0, h], scale, causal))
+    _check_grads(grads, ref, extra, f"{kind} step")
+
+
+@pytest.mark.parametrize("kind,N,d,causal", BWD_CASES)
+def test_backward_end_to_end(fa, kind, N, d, causal):
+    """Forward then backward on the GPU from the original inputs, against the
+    oracle's exact gradients. The forward's O and L are first checked against
+    the oracle at the stated tolerances; the gradient bound then adds what
+    those tolerances can do to the backward (through D = rowsum(dO * O) and
+    P = exp(S - L)) and the kernel's bf16 rounding, all from oracle values
+    (tests/gpu_util.saved_inputs_bound)."""
     import torch
     dev, vals = _inputs(kind, 1, 2, N, d, 1300 + N + d)
     scale = 1.0 / np.sqrt(d)
@@ -83,23 +151,11 @@ def test_backward_against_oracle(fa, kind, N, d, causal):
     o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=scale)
     grads = fa.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=causal, scale=scale)
     torch.cuda.synchronize()
-    # Reference: the backward step on the forward's own saved O (bf16) and L.
-    # With these keys |dQ| reaches about 20, and the bf16 rounding of O alone
-    # moves D = rowsum(dO * O), hence dQ, by more than one bf16 spacing.
-    # The bound adds the propagated bf16 rounding of P and dS (grad_rounding_bound),
-    # which here exceeds one spacing of the result where dS K cancels.
-    oh, lh = host(o), host(lse)
-    ref = A.backward_from_saved(vals["q"], vals["k"], vals["v"], oh, lh, vals["do"], scale, causal)
-    extra = [np.empty_like(r) for r in ref]
-    for h in range(2):
-        b = grad_rounding_bound(vals["q"][0, h], vals["k"][0, h], vals["v"][0, h], oh[0, h], lh[0, h],
-                                vals["do"][0, h], scale, causal)
-        for t, x in zip(extra, b):
-            t[0, h] = x
-    for name, g, r, ex in zip(("dQ", "dK", "dV"), grads, ref, extra):
-        g = host(g)
-        assert np.all(np.isfinite(g)), f"{name} not finite"
-        bound = np.maximum(2e-2, bf16_ulp(r)) + ex
-        err = max_abs(g, r)
-        print(f"{kind} {name}: max-abs {err:.2e} (max|ref| {np.max(np.abs(r)):.3g})")
-        assert bool(np.all(np.abs(g - r) <= bound)), f"{name} max-abs {err:.3e}"
+    o_ref, l_ref = A.forward(vals["q"], vals["k"], vals["v"], scale, causal)
+    eo, el = max_abs(host(o), o_ref), max_abs(host(lse), l_ref)
+    print(f"{kind} forward: O {eo:.2e} LSE {el:.2e}")
+    assert eo <= TOL_O, f"O max-abs {eo:.3e}"
+    assert el <= TOL_L, f"LSE max-abs {el:.3e}"
+    ref = A.backward(vals["q"], vals["k"], vals["v"], vals["do"], scale, causal)
+    extra = _head_bounds(saved_inputs_bound, vals, 2, lambda h: (vals["do"][0, h], scale, causal, TOL_O, TOL_L))
+    _check_grads(grads, ref, extra, f"{kind} end-to-end")
