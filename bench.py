@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+PEAK_FP32_MFMA_TFLOPS = 157.3 # MI355X dense fp32 matrix, published
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_tiled_attention_12_amd", "csrc")
 
@@ -61,16 +62,29 @@ def load_traffic(kernel_key, files, per_launch_units):
     return ent.get("hbm_bytes_per_launch")
 
 
+def host_info():
+    """Host cores and the BLAS library numpy runs the oracle's products on."""
+    info = {"host_cpus": os.cpu_count()}
+    try:
+        from threadpoolctl import threadpool_info
+        pools = threadpool_info()
+        blas = [p for p in pools if p.get("user_api") == "blas"]
+        info["blas"] = "; ".join(f"{p.get('internal_api')} {p.get('version')}"
+                                 + (f" ({p['threading_layer']})" if p.get("threading_layer") else "")
+                                 for p in blas) or "unknown"
+        info["blas_threads"] = max([p.get("num_threads", 1) for p in blas] or [1])
+    except Exception:  # pragma: no cover
+        info["blas"] = "unknown"
+        info["blas_threads"] = os.cpu_count() or 1
+    return info
+
+
 def cpu_baseline(heads: int):
     """The float64 oracle, timed on this host on a bounded sample of the workload."""
     import numpy as np
     import seeded_inputs as si
     from oracle import attention as A
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    hi = host_info()
     w = si.workload(4)
     rng = np.random.default_rng(w.seed)
     shape = (w.N, w.d)
@@ -81,9 +95,105 @@ def cpu_baseline(heads: int):
         A.backward(x["q"], x["k"], x["v"], x["do"], w.scale, True)
     dt = time.perf_counter() - t0
     flops = heads * (attention_flops(1, 1, w.N, w.d, True) + attention_flops(1, 1, w.N, w.d, True, True))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(hi["blas_threads"]), "kind": "oracle",
             "sample": f"{heads} head(s) of the N=16384 d=128 causal workload, forward + backward, "
-                      f"float64 numpy, {dt:.1f} s"}
+                      f"float64 numpy, {dt:.1f} s",
+            "host_cpus": hi["host_cpus"], "blas": hi["blas"]}
+
+
+def oracle_configs():
+    """The float64 oracle timed once per workload on this host (a baseline, not a target).
+
+    Heads are independent, so where a whole workload would take long a seeded
+    subset of its heads is timed and the time scaled by heads / subset.
+    FLOPs follow the same convention as the GPU figures (the oracle also
+    computes the masked half of a causal score matrix). The fp8 workload's
+    leg is its full oracle path: quantisation (rotated Q, K), the tiled fp8
+    emulation, the per-tensor fp8 baseline emulation and the exact forward.
+    """
+    import numpy as np
+    import seeded_inputs as si
+    from oracle import attention as A
+    from oracle import fp8 as F
+    res = {"host": host_info()}
+    subset = {1: 1, 2: 96, 3: 8, 4: 2, 5: 1}   # heads timed
+    for k in (1, 2, 3, 4, 5):
+        w = si.workload(k)
+        nh = subset[k]
+        # a sample of nh heads (B = 1, H = nh) drawn with the workload's seed
+        # and recipe; workload 2 is timed whole
+        ws = w.resized(B=1, H=nh) if w.B * w.H > nh else w
+        x = si.make_inputs(ws)
+        t0 = time.perf_counter()
+        if k == 5:
+            q8, sq, _ = F.quantize(x["q"], 64, x["rot"])
+            k8, sk, _ = F.quantize(x["k"], 64, x["rot"])
+            v8, sv, _ = F.quantize(x["v"], 64)
+            F.fp8_attention_tiled(q8, sq, k8, sk, v8, sv, w.scale, w.causal)
+            q8, sq, _ = F.quantize(x["q"], 0)
+            k8, sk, _ = F.quantize(x["k"], 0)
+            v8, sv, _ = F.quantize(x["v"], 0)
+            F.fp8_attention_tiled(q8, sq, k8, sk, v8, sv, w.scale, w.causal)
+            A.forward(x["q"], x["k"], x["v"], w.scale, w.causal)
+        else:
+            A.forward(x["q"], x["k"], x["v"], w.scale, w.causal)
+            if w.backward:
+                A.backward(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal)
+        dt = time.perf_counter() - t0
+        heads_done = ws.B * ws.H
+        total_heads = w.B * w.H
+        full_s = dt * total_heads / heads_done
+        flops = attention_flops(w.B, w.H, w.N, w.d, w.causal, False)
+        if w.backward:
+            flops += attention_flops(w.B, w.H, w.N, w.d, w.causal, True)
+        res[f"workload_{k}"] = {"shape": [w.B, w.H, w.N, w.d], "dtype": w.dtype, "causal": w.causal,
+                                "legs": "fp8 path (quantise, block + per-tensor emulation, exact forward)"
+                                if k == 5 else ("forward + backward" if w.backward else "forward"),
+                                "heads_timed": heads_done, "seconds_timed": round(dt, 3),
+                                "seconds_full": round(full_s, 4), "extrapolated": heads_done < total_heads,
+                                "useful_gflops": round(flops / full_s / 1e9, 2)}
+        print(json.dumps({f"workload_{k}": res[f"workload_{k}"]}), flush=True)
+    return res
+
+
+def configs_section(fa, which=(1, 2, 3)):
+    """Forward-only workloads 1-3 on their seeded inputs: median of timed reps.
+
+    5 warm-up calls, then 100 timed calls (workloads 1 and 2) or 20
+    (workload 3), each between two events on the launch stream.
+    """
+    import numpy as np
+    import torch
+    import seeded_inputs as si
+    res = {}
+    for k in which:
+        w = si.workload(k)
+        x = si.make_inputs(w, names=("q", "k", "v"))
+        if w.dtype == "f32":
+            t = {n: torch.from_numpy(x[n]).cuda() for n in "qkv"}
+        else:
+            t = {n: torch.from_numpy(x[n + "_bits"].view(np.int16)).view(torch.bfloat16).cuda() for n in "qkv"}
+        del x
+        o = torch.empty_like(t["q"])
+        lse = torch.empty((w.B, w.H, w.N), device="cuda", dtype=torch.float32)
+        reps = 100 if k in (1, 2) else 20
+        for _ in range(5):
+            fa.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in ev:
+            e[0].record()
+            fa.fwd(t["q"], t["k"], t["v"], causal=w.causal, scale=w.scale, out=o, lse=lse)
+            e[1].record()
+        torch.cuda.synchronize()
+        ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+        tf = attention_flops(w.B, w.H, w.N, w.d, w.causal) / (ms * 1e-3) / 1e12
+        peak = PEAK_FP32_MFMA_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        res[f"workload_{k}"] = {"shape": [w.B, w.H, w.N, w.d], "dtype": w.dtype, "causal": w.causal,
+                                "fwd_ms": round(ms, 4), "fwd_tflops": round(tf, 2),
+                                "frac_of_peak": round(tf / peak, 4), "peak_tflops": peak}
+        del t, o, lse
+    return res
 
 
 def fp8_section(fa, steps: int, warmup: int):
@@ -281,6 +391,11 @@ def main():
     ap.add_argument("--fp8-only", action="store_true",
                     help="time only the fp8 workload and print its figures as one JSON line")
     ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--no-configs", action="store_true", help="skip the forward timing of workloads 1-3")
+    ap.add_argument("--config-only", type=int, default=0, metavar="K",
+                    help="time only the forward of workload K (1, 2 or 3) and print its figures")
+    ap.add_argument("--oracle-configs", action="store_true",
+                    help="time the float64 oracle once per workload on this host (no GPU needed)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the warm-up, copy MIB MiB device-to-device once (a transfer of known "
                          "size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -291,6 +406,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.oracle_configs:
+        print(json.dumps({"oracle_configs": oracle_configs()}), flush=True)
+        return
+
     import numpy as np
     import torch
     import exact_tiled_attention_12_amd as fa
@@ -300,8 +419,19 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     fa.load()
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, device="cuda", dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.fp8_only:
         print(json.dumps({"fp8": fp8_section(fa, args.steps, args.warmup)}), flush=True)
+        return
+    if args.config_only:
+        print(json.dumps({"configs": configs_section(fa, (args.config_only,))}), flush=True)
         return
     w = si.workload(4)
     B, H, N, d = w.B, w.H, w.N, w.d
@@ -318,14 +448,6 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), device=dev, dtype=torch.uint8)
     do_bwd = not args.fwd_only
-    if args.calibrate_copy > 0:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, device=dev, dtype=torch.uint8)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     def step(ev=None):
         # Events on torch's current stream, which is the stream the library launches on.
@@ -413,6 +535,9 @@ def main():
     if not args.no_fp8:
         torch.cuda.empty_cache()
         out["fp8"] = fp8_section(fa, args.steps, args.warmup)
+    if not args.no_configs:
+        torch.cuda.empty_cache()
+        out["configs"] = configs_section(fa)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_heads)
     print(json.dumps(out), flush=True)
