@@ -171,7 +171,8 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
     """dQ, dK, dV of sum(O * dO), recomputing P from LSE. bf16 or float32.
 
     deterministic=True (bf16 only) calls fa_bwd_det: dQ is reduced over key
-    tiles in a fixed order, so every output is bit-identical from run to run.
+    tiles in a fixed order (counter-ordered adds, O(N) workspace), so every
+    output is bit-identical from run to run.
     k and v may have fewer heads than q (bf16, fa_bwd_gqa); dk and dv then
     have k's shape and sum over each K/V head's query heads.
     """

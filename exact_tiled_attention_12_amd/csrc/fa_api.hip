@@ -117,8 +117,6 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   if (rc) return rc;
   rc = check_kv_heads(H, H_kv);
   if (rc) return rc;
-  if (det && (size_t)fa::bwd_row_tiles(N) * fa::kBwdPartFloats * 4 > (1u << 31))
-    return fail(FA_ERR_UNSUPPORTED, "sequence too long for the fixed-order backward (N = %d)", N);
   const size_t need = det ? fa_bwd_det_workspace_bytes(B, H, N, d, causal)
                      : H_kv < H ? fa_bwd_gqa_workspace_bytes(B, H, H_kv, N, d) : fa_bwd_workspace_bytes(B, H, N, d);
   if (ws == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
@@ -139,15 +137,20 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.N = N; a.scale = scale; a.c = log2e_scale(scale);
   a.H = H; a.group = H / H_kv; a.B = B;
+  a.dq_acc = (float*)ws;
+  a.dvec = (float*)((char*)ws + align256((size_t)B * H * N * d * 4));
   if (det) {
-    // D first, then the partial tiles.
-    a.dvec = (float*)ws;
-    a.dq_part = (float*)((char*)ws + align256((size_t)B * H * N * 4));
-  } else {
-    a.dq_acc = (float*)ws;
-    a.dvec = (float*)((char*)ws + align256((size_t)B * H * N * d * 4));
+    // fixed order: for d = 64 a second dQ accumulator (one per key half),
+    // then D, then the per-query-tile counters and the error flag
+    const size_t n_cnt = (size_t)B * H * fa::bwd_row_tiles(N) * fa::kBwdSlots;
+    const size_t acc = align256((size_t)B * H * N * 128 * 4);
+    a.dvec = (float*)((char*)ws + acc);
+    a.dq_cnt = (int*)((char*)ws + acc + align256((size_t)B * H * N * 4));
+    a.dq_err = a.dq_cnt + n_cnt;
+    a.n_cnt = (int)(n_cnt + 1);
+  } else if (H_kv < H) {
     // grouped K/V heads: float32 dK, dV per query head after D
-    if (H_kv < H) a.dkv_part = (float*)((char*)ws + fa_bwd_workspace_bytes(B, H, N, d));
+    a.dkv_part = (float*)((char*)ws + fa_bwd_workspace_bytes(B, H, N, d));
   }
   return launched(fa::launch_bwd(dt, d, causal, a, B, H, stage_mask, (hipStream_t)stream), "attention backward");
 }
@@ -198,11 +201,14 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
 }
 
 size_t fa_bwd_det_workspace_bytes(int B, int H, int N, int d, int causal) {
-  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
-  const size_t parts = (size_t)fa::bwd_det_parts(N, causal ? 1 : 0);
-  const size_t bh = (size_t)B * H;
-  if (parts > SIZE_MAX / 4 / fa::kBwdPartFloats / bh) return 0;
-  return align256(bh * N * 4) + align256(bh * parts * fa::kBwdPartFloats * 4);
+  (void)causal;   // the same for both masks
+  if (fa_bwd_workspace_bytes(B, H, N, d) == 0) return 0;
+  // float32 dQ accumulators (d = 128: one; d = 64: one per key half, B H N
+  // 64 floats each), D, then kBwdSlots counters per (batch, head, 32-row
+  // query tile) and the error flag
+  const size_t bhn = (size_t)B * H * N;
+  return align256(bhn * 128 * 4) + align256(bhn * 4) +
+         align256(((size_t)B * H * fa::bwd_row_tiles(N) * fa::kBwdSlots + 1) * 4);
 }
 
 int fa_bwd_det(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

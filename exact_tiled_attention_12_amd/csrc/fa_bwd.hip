@@ -8,7 +8,8 @@
 // from Q, K and the saved log-sum-exp L, and
 //   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
 //   dK = scale dS^T Q,  dQ = scale dS K      (five matrix products per tile).
-// dQ is summed across key tiles with float32 atomics (the pages' dQ atomics).
+// dQ is summed across key tiles with float32 atomics (the pages' dQ atomics),
+// or, in the bf16 fixed-order mode, in ascending key-tile order.
 //
 // Three launches:
 //   1. preprocess: D_i = sum_c dO_ic O_ic (float32) and zero the float32 dQ
@@ -81,12 +82,17 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a, long long 
     const T* gp = (const T*)&gv;
 #pragma unroll
     for (int e = 0; e < E; ++e) part += (float)op[e] * (float)gp[e];
-    if (a.dq_acc != nullptr) {   // (the fixed-order mode has no accumulator)
-      float* acc = a.dq_acc + off;
+    float* acc = a.dq_acc + off;
 #pragma unroll
-      for (int e = 0; e < E; e += 4) *(f32x4*)(acc + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < E; e += 4) *(f32x4*)(acc + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+    // fixed order, d = 64: the second key half's accumulator
+    if (D == 64 && a.dq_cnt != nullptr) {
+#pragma unroll
+      for (int e = 0; e < E; e += 4) *(f32x4*)(acc + rows * D + e) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  // Fixed-order mode: clear the per-tile counters and the error flag.
+  if (a.dq_cnt != nullptr && gid < a.n_cnt) a.dq_cnt[gid] = 0;
   // Sum over the CPR consecutive lanes that hold one row (CPR divides 64).
 #pragma unroll
   for (int sh = 1; sh < CPR; sh <<= 1) part += __shfl_xor(part, sh, 64);
@@ -99,7 +105,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, long long n
   using T = typename Tr::T;
   const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n4) return;
-  const f32x4 v = *(const f32x4*)(a.dq_acc + 4 * i) * a.scale;
+  f32x4 acc = *(const f32x4*)(a.dq_acc + 4 * i);
+  // fixed order, d = 64: key half 0's accumulator plus key half 1's
+  if (D == 64 && a.dq_cnt != nullptr) acc += *(const f32x4*)(a.dq_acc + 4 * (i + n4));
+  f32x4 v = acc * a.scale;
+  // Fixed-order mode: a wait that ran out left the order (and maybe the
+  // sum) unknown; dq becomes NaN so that the failure cannot pass unseen.
+  if (a.dq_err != nullptr && *(const volatile int*)a.dq_err != 0) v = f32x4{NAN, NAN, NAN, NAN};
   T* dst = (T*)a.dq + 4 * i;
   if constexpr (sizeof(T) == 2) {
     u32x2 w;
@@ -109,61 +121,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, long long n
   } else {
     *(f32x4*)dst = v;
   }
-}
-
-// ------------------------------------------------- fixed-order dQ finish
-// The partial rows of key tile kt (per batch-head, after those of key tiles
-// 0 .. kt-1) are the dQ contributions of its 256 keys to the query rows it
-// visits, row-major [rows][d] from the first visited row (causal: row
-// kt * 256) to the last tile's end; for d = 64 one such block per key half.
-//
-// One thread per (row, 4 columns): dq = scale * (sum over kt = 0, 1, ... in
-// that order, key half 0 before key half 1), rounded to bf16 once.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dq_det_kernel(BwdArgs a, long long n4) {
-  constexpr int C4 = D / 4;                      // 4-float groups per row
-  constexpr int HALVES = D == 64 ? 2 : 1;
-  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n4) return;
-  const int N = a.N;
-  const long long row = i / C4;
-  const int c = (int)(i % C4) * 4;
-  const long long bh = row / N;
-  const int q = (int)(row - bh * N);
-  const int n_qt = bwd_row_tiles(N);
-  // Key tiles whose visits reach row q: all, or (causal) those with kt * 256 <= q's tile start.
-  const int n_kt = CAUSAL ? min(bwd_key_tiles(N), q / kBwdKeyTile + 1) : bwd_key_tiles(N);
-  const float* head = a.dq_part + (size_t)bh * (size_t)bwd_det_parts(N, CAUSAL) * kBwdPartFloats;
-  auto part = [&](int kt, int h) -> f32x4 {
-    const int first = CAUSAL ? kt * (kBwdKeyTile / kBwdRowTile) : 0;   // first visited query tile
-    const size_t rows_kt = (size_t)(n_qt - first) * kBwdRowTile;        // rows per key half
-    const float* p = head + (size_t)bwd_part_offset(N, CAUSAL, kt) * kBwdPartFloats +
-                     ((size_t)h * rows_kt + (size_t)(q - first * kBwdRowTile)) * D + c;
-    return __builtin_nontemporal_load((const f32x4*)p);
-  };
-  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-  // Loads of four key tiles are issued before their adds; the adds keep the
-  // ascending order.
-  int kt = 0;
-  for (; kt + 4 <= n_kt; kt += 4) {
-    f32x4 v[4][HALVES];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int h = 0; h < HALVES; ++h) v[u][h] = part(kt + u, h);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int h = 0; h < HALVES; ++h) sum += v[u][h];
-  }
-  for (; kt < n_kt; ++kt)
-#pragma unroll
-    for (int h = 0; h < HALVES; ++h) sum += part(kt, h);
-  const f32x4 v = sum * a.scale;
-  u32x2 w;
-  w[0] = pack_bf16x2(v[0], v[1]);
-  w[1] = pack_bf16x2(v[2], v[3]);
-  *(u32x2*)((__bf16*)a.dq + row * D + c) = w;
 }
 
 // ------------------------------------- grouped-query dK, dV chunk sum
@@ -456,13 +413,6 @@ hipError_t run(int causal, BwdArgs a, int B, int H, int stage_mask, hipStream_t 
   if (stage_mask & 4) {
     const long long n4 = rows * D / 4;
     const int blocks = (int)((n4 + kThreads - 1) / kThreads);
-    if constexpr (sizeof(typename Tr::T) == 2) {
-      if (a.dq_part != nullptr) {
-        if (causal) hipLaunchKernelGGL((bwd_dq_det_kernel<D, true>), dim3(blocks), dim3(kThreads), 0, s, a, n4);
-        else hipLaunchKernelGGL((bwd_dq_det_kernel<D, false>), dim3(blocks), dim3(kThreads), 0, s, a, n4);
-        return hipGetLastError();
-      }
-    }
     hipLaunchKernelGGL((bwd_dq_kernel<Tr, D>), dim3(blocks), dim3(kThreads), 0, s, a, n4);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

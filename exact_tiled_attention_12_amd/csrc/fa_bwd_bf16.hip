@@ -27,6 +27,17 @@
 //     atomics; query tiles are visited from the last down to the diagonal so
 //     that the workgroups of a (batch, head) add to the same dQ rows at the
 //     same time and the atomics stay in L2;
+//   * fixed-order mode ("FlashAttention v1～v4 完整进化史", v4 part 4: the
+//     deterministic backward orders the reduction across workgroups with
+//     semaphores): a wave adds its dQ slice to a query tile only after a
+//     per-(query tile, slice) counter shows that every earlier key tile has
+//     added its own, and bumps the counter once its adds are complete, so
+//     the adds to every dQ element happen in ascending key-tile order. A workgroup only waits on key tiles of its own (batch,
+//     head) with smaller workgroup ids, which the hardware dispatches first
+//     (ids go to the XCDs round-robin and each XCD starts its workgroups in
+//     id order; the tiles of a (batch, head) share one XCD); every wait is
+//     bounded, and a wait that runs out raises an error flag that turns dq
+//     into NaN instead of hanging;
 //   * one wave per SIMD means the wave itself must keep the matrix core fed:
 //     the products of a tile run in one interleaved stream (S and dP, dV and
 //     dK, and dQ of the previously visited tile), operands are read ahead,
@@ -47,7 +58,11 @@ constexpr int kKW = 64;              // keys per wave
 constexpr int kBC = kKW * kWaves;    // keys per workgroup
 constexpr int kBR = 32;              // query rows per tile
 constexpr int kStages = 3;           // query-tile ring depth
-static_assert(kBC == kBwdKeyTile && kBR == kBwdRowTile, "partial-tile layout of the fixed-order dQ");
+static_assert(kBC == kBwdKeyTile && kBR == kBwdRowTile && kWaves == kBwdSlots, "counter layout of the fixed-order dQ");
+// Polls of the fixed-order counters a wave may spend in waits over the whole
+// kernel before giving up (each poll is a device-scope load plus a short
+// sleep: a second or two in all).
+constexpr unsigned kSpinLimit = 1u << 20;
 
 #define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -110,8 +125,8 @@ __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 #define INL __attribute__((always_inline)) __device__
 
-// DET: dQ contributions go to partial tiles (plain stores, one tile per
-// visited (key tile, query tile) pair) instead of float32 atomics.
+// DET: dQ contributions are added to the accumulator in ascending key-tile
+// order (the float32 atomics of each query tile ordered by a counter).
 // Grouped K/V heads (a.group > 1): one query head per workgroup with its
 // group's K/V head; float32 dK and dV of each query head go to the workspace
 // for a fixed-order sum over the group.
@@ -200,20 +215,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
   const int k0 = kt * kBC;
   const int kw0 = k0 + wave * kKW;
-  // dQ destination, addressed by query row: the float32 accumulator of the
-  // head, or (DET) this key tile's partial rows. Those hold rows from the
-  // first visited query tile on (and, for d = 64, one block of them per key
-  // half), so the base is moved back by the rows before that tile.
+  // dQ destination, addressed by query row: the float32 accumulator of the head.
   const int n_qt = (N + kBR - 1) / kBR;
   const int qt_begin = CAUSAL ? k0 / kBR : 0;
   const int nt = n_qt - qt_begin;   // query tiles visited per query head (>= 1)
   const int nvis = nt;              // visits: query tile n_qt - 1 - i at visit i
-  const __amdgpu_buffer_rsrc_t rdq =
-      DET ? make_rsrc(a.dq_part + ((size_t)bh * (size_t)bwd_det_parts(N, CAUSAL) +
-                                   (size_t)bwd_part_offset(N, CAUSAL, kt)) * kBwdPartFloats +
-                          (size_t)(D == 64 ? (wave >> 1) : 0) * nt * kBR * D - (size_t)qt_begin * kBR * D,
-                      (unsigned)n_qt * kBR * D * 4)
-          : make_rsrc(a.dq_acc + qbase, (unsigned)N * D * 4);
+  // (Fixed order, d = 64: each key half has an accumulator of its own, the
+  // second one B H N d floats after the first; the finish pass adds them.)
+  const size_t dq_half = DET && D == 64 && wave >= 2 ? (size_t)a.B * a.H * (size_t)N * D : 0;
+  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(a.dq_acc + dq_half + qbase, (unsigned)N * D * 4);
   const unsigned kt_a = (unsigned)(uintptr_t)LDS(unsigned char, kt_s);
   const unsigned rg_a = (unsigned)(uintptr_t)LDS(unsigned char, rg_s);
 
@@ -311,26 +321,84 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     t.v[3] = tr_read(kt_s + (t_lane[1] ^ (64u * db_q)) + kc * 16 * C::RB);
     return t;
   };
-  // dQ atomics (DET: stores) of the slice, rows of the query tile of visit
-  // `visit`, at the rows' own offsets in rdq. A tile that does not exist (or
-  // rows past N) gets offsets past the buffer: the operations are no-ops, so
-  // the number of memory operations per tile is the same everywhere.
-  auto dq_atomic = [&](const f32x16& acc, int visit, bool live, int r) INL {
+  // dQ atomics of the slice, rows of the query tile of visit `visit`, at the
+  // rows' own offsets in rdq. A tile that does not exist (or rows past N)
+  // gets offsets past the buffer: the operations are no-ops, so the number
+  // of memory operations per tile is the same everywhere.
+  auto dq_off = [&](int visit, bool live, int r) INL -> unsigned {
     const int q = (n_qt - 1 - visit) * kBR + 8 * (r >> 2) + 4 * hh + (r & 3);
-    const unsigned off = live && q < N ? ((unsigned)q * D + db_q * 32 + l32) * 4 : 0x80000000u;
-    if constexpr (DET) {
-      // (Bit cast of a copy: hipcc compiled a bit cast applied directly to an
-      // element of a vector variable as a cast of its first element.)
-      const float x = acc[r];
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), rdq, off, 0, 0);
-    } else {
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rdq, off, 0, 0);
-    }
+    return live && q < N ? ((unsigned)q * D + db_q * 32 + l32) * 4 : 0x80000000u;
+  };
+  auto dq_atomic = [&](const f32x16& acc, int visit, bool live, int r) INL {
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rdq, dq_off(visit, live, r), 0, 0);
   };
   constexpr int NDQ = 16;   // dQ memory operations per visit
   auto dq_atomics = [&](const f32x16& acc, int visit, bool live) INL {
 #pragma unroll
     for (int r = 0; r < NDQ; ++r) dq_atomic(acc, visit, live, r);
+  };
+
+  // ---- fixed-order dQ (DET). Each wave adds to elements no other wave of
+  // the workgroup touches (d = 128: its column block; d = 64: its column
+  // block of its key half's accumulator), so each has a counter (slot) of
+  // its own per query tile and waits only on the same wave of lower key
+  // tiles: key tile kt's add to a query tile is the kt-th one there.
+  const int dq_turn = kt;
+  // A device-coherent read of the counter of the tile of `visit` (sc1: the
+  // same cache policy as a device-scope atomic load), addressed by scalar
+  // registers only, so it holds no vector register but its result.
+  const __amdgpu_buffer_rsrc_t rcnt = make_rsrc(a.dq_cnt + (size_t)bhc * n_qt * kBwdSlots, (unsigned)n_qt * kBwdSlots * 4);
+  auto dq_peek = [&](int visit) INL -> int {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rcnt, 0, ((n_qt - 1 - visit) * kBwdSlots + wave) * 4, 16);
+  };
+  // Wait until the earlier contributions to the tile of `visit` are added:
+  // the counter is read with device-coherent loads, and this wave's adds are
+  // issued only after the load that saw it reach dq_turn has returned. The
+  // poll is one assembly block (the load, a compare, a short sleep), so the
+  // wait adds no loop to the control flow around the pipelined body (a loop
+  // there made the register allocator spill). The wave's polls share one
+  // budget over the whole kernel: once it is spent the error flag is set
+  // and later waits give up after a single poll, so a wave never polls
+  // more than kSpinLimit + visits times.
+  unsigned poll_budget = kSpinLimit;
+  auto dq_acquire = [&](int visit) INL {
+    const int soff = ((n_qt - 1 - visit) * kBwdSlots + wave) * 4;
+    int seen, tmp;
+    asm volatile(
+        "1:\n\t"
+        "buffer_load_dword %[t], off, %[r], %[o] sc1\n\t"
+        "s_waitcnt vmcnt(0)\n\t"
+        "v_readfirstlane_b32 %[v], %[t]\n\t"
+        "s_cmp_ge_i32 %[v], %[want]\n\t"
+        "s_cbranch_scc1 2f\n\t"
+        "s_cmp_eq_u32 %[n], 0\n\t"
+        "s_cbranch_scc1 2f\n\t"
+        "s_sub_u32 %[n], %[n], 1\n\t"
+        "s_sleep 1\n\t"
+        "s_branch 1b\n"
+        "2:"
+        : [t] "=&v"(tmp), [v] "=&s"(seen), [n] "+s"(poll_budget)
+        : [r] "s"(rcnt), [o] "s"(soff), [want] "s"(dq_turn)
+        : "memory", "scc");
+    (void)tmp;
+    if (seen < dq_turn) __hip_atomic_store(a.dq_err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // The counter of the tile of `visit` as read during that visit (dq_seen);
+  // only if it was not yet this key tile's turn does the wave poll.
+  int dq_seen = 0;
+  auto dq_wait = [&](int visit) INL {
+    if (__builtin_amdgcn_readfirstlane(dq_seen) < dq_turn) dq_acquire(visit);
+  };
+  // Publish this wave's adds to the tile of `visit`: the caller has waited
+  // for every memory operation of the wave to complete (vmcnt 0), so the
+  // float adds are done at the device-wide point where atomics are
+  // performed before the counter moves. The accumulator is only ever
+  // touched by atomics until the kernel ends, so no cache needs writing
+  // back or invalidating: the order of the adds is all that is published.
+  auto dq_release = [&](int visit) INL {
+    asm volatile("" ::: "memory");
+    if (lane == 0)
+      __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, rcnt, 0, ((n_qt - 1 - visit) * kBwdSlots + wave) * 4, 0);
   };
 
   __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS));   // K tile, V operands, query tile 0
@@ -345,14 +413,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   for (int i = 0; i < nvis; ++i) {
     const int qt = n_qt - 1 - i;
     if (i > 0) {
-      // Memory operations issued after visit i's own copies: (i >= 2) the NDQ
-      // dQ operations of visit i-2, then the copies of visit i+1 and the NDQ
-      // dQ operations of visit i-1.
-      if (i == 1)
-        __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + NDQ));
-      else
-        __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + 2 * NDQ));
-      lds_barrier();
+      if constexpr (DET) {
+        // Only the NDQ dQ atomics of visit i-1 may stay in flight: the
+        // copies of visits i and i+1, the atomics of visit i-2 (those of
+        // visit i-3's tile, published here) and the counter read of visit
+        // i-1 have landed. That read decides whether this visit's adds (to
+        // visit i-1's tile) may go ahead or must wait.
+        __builtin_amdgcn_s_waitcnt(wait_vm(NDQ));
+        lds_barrier();
+        if (i >= 3) dq_release(i - 3);
+        dq_wait(i - 1);
+      } else {
+        // Memory operations issued after visit i's own copies: (i >= 2) the NDQ
+        // dQ operations of visit i-2, then the copies of visit i+1 and the NDQ
+        // dQ operations of visit i-1.
+        if (i == 1)
+          __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + NDQ));
+        else
+          __builtin_amdgcn_s_waitcnt(wait_vm(C::R_LOADS + 2 * NDQ));
+        lds_barrier();
+      }
     }
 
     const int q0 = qt * kBR;
@@ -510,6 +590,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
           dq_acc = mma(join(qop[m % 2].v[0], qop[m % 2].v[1]), join(qop[m % 2].v[2], qop[m % 2].v[3]), dq_acc);
         }
       } else {
+        // Fixed order: read the counter of this visit's own tile now (the
+        // next visit adds to it); its value is needed only after the next
+        // barrier, so the read costs no wait.
+        if constexpr (DET) {
+          if (step == QS) dq_seen = dq_peek(i);
+        }
         // memory operations r in [lo, hi) of the NDQ, split evenly over steps QS .. NS-1
         constexpr int NA = NS - QS;
         const int lo = (step - QS) * NDQ / NA, hi = (step - QS + 1) * NDQ / NA;
@@ -521,7 +607,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   }
 
   // dQ of the last visited tile.
-  lds_barrier();
+  if constexpr (DET) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(NDQ));
+    lds_barrier();
+    if (nvis >= 3) dq_release(nvis - 3);
+    dq_wait(nvis - 1);
+  } else {
+    lds_barrier();
+  }
   {
     const unsigned char* sb = dsb((nvis - 1) & 1);
     Tr4 qop[3];
@@ -536,6 +629,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     dq_atomics(dq_acc, nvis - 1, true);
+    if constexpr (DET) {
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      if (nvis >= 2) dq_release(nvis - 2);
+      dq_release(nvis - 1);
+    }
   }
 
   // Epilogue: dK = scale * acc, dV = acc (lanes = d, rows = keys); rows past N dropped.
@@ -601,7 +699,7 @@ hipError_t launch_bwd_bf16_main(int d, int causal, BwdArgs a, int B, int H, hipS
   const long long grid = a.cu_seqlens != nullptr ? (long long)a.n_seq * H * a.n_tiles
                                                  : (long long)B * H * a.n_tiles;
   a.remap = grid % 8 == 0 ? 1 : 0;
-  const bool det = a.dq_part != nullptr;
+  const bool det = a.dq_cnt != nullptr;
   if (d == 64) {
     if (causal) det ? launch_main<64, true, true>(a, grid, s) : launch_main<64, true, false>(a, grid, s);
     else det ? launch_main<64, false, true>(a, grid, s) : launch_main<64, false, false>(a, grid, s);

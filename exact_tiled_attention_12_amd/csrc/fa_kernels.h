@@ -37,9 +37,14 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;  // [B,H,N,d] float32 workspace (nullptr in the fixed-order mode)
+  float* dq_acc;  // [B,H,N,d] float32 workspace: the dQ accumulator
   float* dvec;    // [B,H,N] float32 workspace: D = rowsum(dO * O)
-  float* dq_part; // fixed-order mode: dQ partial tiles (bwd_det_parts), else nullptr
+  // Fixed-order mode (bf16, one K/V head per query head): per (batch, head,
+  // 32-row query tile) kBwdSlots counters of the key-tile contributions added
+  // to that tile's dQ rows so far, then one error flag; nullptr otherwise.
+  int* dq_cnt;
+  int* dq_err;
+  int n_cnt;      // counters (and the flag) the preprocess pass clears
   int N;
   int n_tiles;    // filled by the launcher
   float scale;
@@ -81,40 +86,23 @@ struct Fp8FwdArgs {
   int remap;      // filled by the launcher
 };
 
-// Fixed-order (deterministic) dQ of the bf16 backward: each 256-key tile
-// stores its dQ contribution to every query row it visits (float32, its own
-// rows: no atomics), and the finish pass adds them per row in ascending
-// key-tile order. Per (batch, head), key tile kt owns a block of
-// bwd_visits(N, causal, kt) tiles of kBwdPartFloats floats, after the blocks
-// of key tiles 0 .. kt-1: its visited rows (32 per query tile, from its first
-// visited tile on) x d, once per key half for d = 64 (the two halves of its
-// keys are summed by different waves).
+// Fixed-order (deterministic) dQ of the bf16 backward: the key tiles of a
+// (batch, head) add their dQ contributions to each 32-row query tile in
+// ascending key-tile order (read, add, write back; no float atomics), each
+// waiting on a counter of that query tile for its predecessor. For d = 128
+// the four waves of a key tile own one 32-column block of dQ each; for
+// d = 64 two waves share a column block, key half 0 before key half 1.
 constexpr int kBwdKeyTile = 256;
 constexpr int kBwdRowTile = 32;
-constexpr int kBwdPartFloats = 4096;   // floats per partial tile (both d)
+constexpr int kBwdSlots = 4;           // counters per query tile
 
 __host__ __device__ inline int bwd_row_tiles(int N) { return (N + kBwdRowTile - 1) / kBwdRowTile; }
-__host__ __device__ inline int bwd_key_tiles(int N) { return (N + kBwdKeyTile - 1) / kBwdKeyTile; }
-// Query tiles key tile kt visits: all of them, or (causal) those at or below
-// the diagonal, i.e. from tile kt * 256 / 32 on.
-__host__ __device__ inline int bwd_visits(int N, int causal, int kt) {
-  return bwd_row_tiles(N) - (causal ? kt * (kBwdKeyTile / kBwdRowTile) : 0);
-}
-// Partial tiles of key tiles 0 .. kt-1 (kt = number of key tiles: all of them).
-__host__ __device__ inline long long bwd_part_offset(int N, int causal, int kt) {
-  const long long r = bwd_row_tiles(N);
-  const long long c = causal ? kBwdKeyTile / kBwdRowTile : 0;
-  return (long long)kt * r - c * ((long long)kt * (kt - 1) / 2);
-}
-__host__ __device__ inline long long bwd_det_parts(int N, int causal) {
-  return bwd_part_offset(N, causal, bwd_key_tiles(N));
-}
 
 hipError_t launch_fwd(DType dt, int d, int causal, FwdArgs a, int B, int H, hipStream_t s);
 hipError_t launch_fwd_bf16(int d, int causal, FwdArgs a, int B, int H, hipStream_t s);
 // stage_mask: 1 = preprocess (D, zero the dQ accumulator), 2 = main, 4 = dQ finish.
-// With a.dq_part set (bf16 only) the dQ accumulator is not used: the main
-// kernel writes partial tiles and the finish pass adds them in a fixed order.
+// With a.dq_cnt set (bf16 only) the main kernel adds to the dQ accumulator in
+// a fixed key-tile order and the preprocess pass also clears the counters.
 hipError_t launch_bwd(DType dt, int d, int causal, BwdArgs a, int B, int H, int stage_mask, hipStream_t s);
 hipError_t launch_bwd_bf16_main(int d, int causal, BwdArgs a, int B, int H, hipStream_t s);
 hipError_t launch_quant_fp8(int d, QuantArgs a, int B, int H, hipStream_t s);

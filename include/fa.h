@@ -63,25 +63,35 @@ enum fa_status {
 };
 
 /* Forward, bf16 inputs and output (bits of bfloat16 in 2-byte elements).
+ * Defined by "6.1 FlashAttention V1详解", sections 3.2 and 5.1 (tiles of K
+ * and V swept with the online max m and sum l, O rescaled as they change)
+ * and "FlashAttention v1～v4 完整进化史", v2 part 1 (O divided by l once at
+ * the end; one statistic L = m + log l saved per row).
  * q, k, v: [B,H,N,d] bf16. o: [B,H,N,d] bf16 (written). lse: [B,H,N] float (written).
  * Scores and the output accumulator are float32; P is rounded to bf16
  * (nearest-even) before it multiplies V; O is rounded to bf16 once. */
 FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, void* stream);
 
-/* Forward, float32 inputs and output. Same contract as fa_fwd; every product
- * and sum is in float32 (P is not rounded). */
+/* Forward, float32 inputs and output ("6.1 FlashAttention V1详解", sections
+ * 3.2 and 5.1; "FlashAttention v1～v4 完整进化史", v2 part 1). Same contract as
+ * fa_fwd; every product and sum is in float32 (P is not rounded). */
 FA_API int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /* Bytes of device workspace fa_bwd / fa_bwd_f32 need: a float32 dQ
  * accumulator [B,H,N,d] and D = rowsum(dO * O) [B,H,N] float32, each
- * rounded up to 256 bytes. Linear in N (no N x N buffer). Returns 0 for
- * invalid sizes. */
+ * rounded up to 256 bytes. Linear in N (no N x N buffer: the backward's
+ * extra memory is O(N), "6.1 FlashAttention V1详解", section 6.3). Returns 0
+ * for invalid sizes. */
 FA_API size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
-/* Backward, bf16. Given the forward's inputs q, k, v, its outputs o and lse,
- * and dout = dL/dO, writes dq, dk, dv = dL/dQ, dL/dK, dL/dV (bf16):
+/* Backward, bf16 ("6.1 FlashAttention V1详解", sections 6.1-6.2: S and P are
+ * recomputed from Q, K and the saved statistic, with D = rowsum(dO * O);
+ * "FlashAttention v1～v4 完整进化史", v4 part 4: five products per tile, dQ
+ * summed across workgroups with atomic adds). Given the forward's inputs
+ * q, k, v, its outputs o and lse, and dout = dL/dO, writes dq, dk, dv =
+ * dL/dQ, dL/dK, dL/dV (bf16):
  *   D_i = sum_c dO_ic O_ic,  P = exp(scale Q K^T - LSE) (recomputed),
  *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,
  *   dK = scale dS^T Q.
@@ -95,7 +105,9 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
            int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /* The stages of fa_bwd, for callers that schedule them themselves (and for
- * timing the main stage alone). fa_bwd runs stage_mask 7 = 1 | 2 | 4:
+ * timing the main stage alone); what they compute is fa_bwd's ("6.1
+ * FlashAttention V1详解", sections 6.1-6.2). fa_bwd runs stage_mask 7 =
+ * 1 | 2 | 4:
  *   1  preprocess: D = rowsum(dO * O) and a zeroed float32 dQ accumulator,
  *      both in the workspace;
  *   2  main: the recompute of P and the five products; writes dk and dv and
@@ -172,13 +184,19 @@ FA_API int fa_bwd_varlen(const void* q, const void* k, const void* v, const void
 FA_API size_t fa_bwd_varlen_workspace_bytes(int total, int H, int H_kv, int d);
 
 /* Fixed-order (deterministic) backward, bf16 ("FlashAttention v1～v4 完整进化史",
- * v4 part 4: a deterministic backward reduces dQ across workgroups in a
- * fixed order). Same arguments, layouts, checks and mathematics as fa_bwd,
- * but dq is bit-identical from run to run: every (256-key tile, 32-row
- * query tile) pair the backward visits writes its float32 dQ contribution
- * to a partial tile of its own (no atomics), and a final pass adds the
- * partials of each row in ascending key-tile order, scales and rounds to
- * bf16 once. dk and dv are bit-identical to fa_bwd's.
+ * v4 part 4: the deterministic backward reduces dQ across workgroups in a
+ * fixed order, ordered with semaphores). Same arguments, layouts, checks and
+ * mathematics as fa_bwd, but dq is bit-identical from run to run: every
+ * 256-key tile adds its float32 dQ contribution to a 32-row query tile only
+ * after a counter of that query tile shows that all lower key tiles have
+ * added theirs (and for d = 64, key half 0 before key half 1), so every dQ
+ * element is summed in ascending key-tile order; the finish pass scales and
+ * rounds to bf16 once. dk and dv are bit-identical to fa_bwd's. Extra memory
+ * stays O(B H N d) ("6.1 FlashAttention V1详解", section 6.3).
+ * A workgroup waits only on workgroups of its own (batch, head) with lower
+ * ids, which are dispatched before it. Each wait is bounded (about a
+ * second); one that runs out sets an error flag in the workspace and the
+ * call then writes NaN to every element of dq (nothing hangs).
  * workspace: device memory of at least
  * fa_bwd_det_workspace_bytes(B,H,N,d,causal) bytes, 256-byte aligned;
  * contents undefined on entry and exit. */
@@ -187,13 +205,15 @@ FA_API int fa_bwd_det(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes,
                       int B, int H, int N, int d, float scale, int causal, void* stream);
 
-/* Bytes of device workspace fa_bwd_det needs: D [B,H,N] float32 plus one
- * 16 KiB float32 partial tile per visited (256-key tile, 32-row query tile)
- * pair, i.e. about 2 B H N^2 bytes (causal: about half of that), each part
- * rounded up to 256 bytes. Returns 0 for invalid sizes. */
+/* Bytes of device workspace fa_bwd_det needs: fa_bwd_workspace_bytes(B, H,
+ * N, d) (the float32 dQ accumulator and D) plus 4 int32 counters per
+ * (batch, head, 32-row query tile) and an int32 error flag, rounded up to
+ * 256 bytes: linear in N, the same for both masks. Returns 0 for invalid
+ * sizes. */
 FA_API size_t fa_bwd_det_workspace_bytes(int B, int H, int N, int d, int causal);
 
-/* Backward, float32 tensors. Same contract as fa_bwd. */
+/* Backward, float32 tensors ("6.1 FlashAttention V1详解", sections 6.1-6.2).
+ * Same contract as fa_bwd. */
 FA_API int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
                const float* dout, float* dq, float* dk, float* dv,
                void* workspace, size_t workspace_bytes,

@@ -130,23 +130,28 @@ def test_fp8_rejects(lib):
                           1, 1, 64, 128, 0.125, 0, None) == _lib.FA_ERR_INVALID
 
 
-def _det_parts(N, causal):
-    """Visited (256-key tile, 32-row query tile) pairs, counted one by one."""
-    n_qt, n_kt = -(-N // 32), -(-N // 256)
-    return sum(1 for kt in range(n_kt) for qt in range(n_qt) if not causal or qt * 32 >= kt * 256)
-
-
-def test_det_workspace_counts_visited_pairs(lib):
+def test_det_workspace_is_linear_in_n(lib):
+    """The fixed-order backward keeps the method's O(N) extra memory ("6.1
+    FlashAttention V1详解", 6.3): float32 dQ accumulators (d = 128: one,
+    which is the plain backward's workspace with D; d = 64: one per key half)
+    and D, plus 4 int32 counters per 32-row query tile and an error flag; the
+    same for both masks."""
     def al(x):
         return (x + 255) // 256 * 256
     for (B, H, N, d, causal) in [(1, 1, 1, 64, 0), (1, 1, 1, 64, 1), (2, 3, 1000, 128, 1), (2, 3, 1000, 64, 0),
                                  (1, 2, 257, 128, 1), (1, 32, 16384, 128, 1), (1, 32, 16384, 128, 0)]:
         got = lib.fa_bwd_det_workspace_bytes(B, H, N, d, causal)
-        assert got == al(4 * B * H * N) + al(B * H * _det_parts(N, causal) * 4096 * 4), (B, H, N, d, causal)
-    # causal keeps only the pairs at or below the diagonal: about half
-    full = lib.fa_bwd_det_workspace_bytes(1, 32, 16384, 128, 0)
-    half = lib.fa_bwd_det_workspace_bytes(1, 32, 16384, 128, 1)
-    assert 0.5 < half / full < 0.52
+        counters = al(4 * (B * H * (-(-N // 32)) * 4 + 1))
+        assert got == al(4 * B * H * N * 128) + al(4 * B * H * N) + counters, (B, H, N, d, causal)
+        if d == 128:
+            assert got == lib.fa_bwd_workspace_bytes(B, H, N, d) + counters
+    # linear in N: doubling N (a multiple of 32) doubles every part but the flag
+    for N in (1024, 4096, 16384):
+        one, two = (lib.fa_bwd_det_workspace_bytes(1, 32, n, 128, 1) for n in (N, 2 * N))
+        assert abs(two - 2 * one) <= 512
+    assert lib.fa_bwd_det_workspace_bytes(1, 32, 16384, 128, 0) == lib.fa_bwd_det_workspace_bytes(1, 32, 16384, 128, 1)
+    # about 4 (d + 1) + 0.5 bytes per row: 270.6 MB at B=1, H=32, N=16384, d=128
+    assert lib.fa_bwd_det_workspace_bytes(1, 32, 16384, 128, 1) < 271e6
     assert lib.fa_bwd_det_workspace_bytes(0, 1, 1, 64, 0) == 0
     assert lib.fa_bwd_det_workspace_bytes(1, 1, 1, 100, 1) == 0
 
@@ -170,9 +175,8 @@ def test_det_backward_rejects(lib):
     assert small < lib.fa_bwd_det_workspace_bytes(1, 1, N, 64, 1)
     assert _bwd_det(lib, N=N, ws_bytes=small) == _lib.FA_ERR_INVALID
     assert "fa_bwd_det_workspace_bytes" in lib.fa_last_error().decode()
-    # the non-causal layout needs more than the causal one
-    assert _bwd_det(lib, N=N, causal=0, ws_bytes=lib.fa_bwd_det_workspace_bytes(1, 1, N, 64, 1)) == \
-        _lib.FA_ERR_INVALID
+    # one byte short of the size
+    assert _bwd_det(lib, N=N, ws_bytes=lib.fa_bwd_det_workspace_bytes(1, 1, N, 64, 1) - 1) == _lib.FA_ERR_INVALID
     assert _bwd_det(lib, dq=A + 64) == _lib.FA_ERR_INVALID
     assert _bwd_det(lib, d=32) == _lib.FA_ERR_UNSUPPORTED
     assert _bwd_det(lib, scale=float("nan")) == _lib.FA_ERR_UNSUPPORTED
