@@ -41,6 +41,9 @@ SIGNATURES = {
     "fa_bwd_det": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
     "fa_bwd_det_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "fa_bwd_noalloc": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
+    "fa_bwd_noalloc_scratch_bytes": (_c_size, []),
     "fa_bwd_f32": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
     "fa_quant_fp8": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),

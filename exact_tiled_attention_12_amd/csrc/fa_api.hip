@@ -4,7 +4,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
+#include <algorithm>
 #include <cstdio>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_kernels.h"
@@ -153,6 +155,40 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
     a.dkv_part = (float*)((char*)ws + fa_bwd_workspace_bytes(B, H, N, d));
   }
   return launched(fa::launch_bwd(dt, d, causal, a, B, H, stage_mask, (hipStream_t)stream), "attention backward");
+}
+
+// ---- scratch of the allocation-free backward (fa_bwd_noalloc).
+//
+// One fixed array per device, resident while the library is loaded. In host
+// code the name `scratch` stands for the host-side shadow, not for the
+// device memory: the device address comes from hipGetSymbolAddress, looked
+// up once per device with that device current, and only that address is
+// ever passed to kernels.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// *out = device address of this device's scratch array; a non-OK status
+// (with the error text set) if it cannot be found.
+int scratch_on_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return FA_OK;
 }
 
 }  // namespace
@@ -308,6 +344,51 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   if (H_kv < H) a.dkv_part = (float*)((char*)workspace + fa_bwd_workspace_bytes(1, H, total, d));
   return launched(fa::launch_bwd(fa::DType::BF16, d, causal, a, 1, H, 7, (hipStream_t)stream),
                   "variable-length attention backward");
+}
+
+size_t fa_bwd_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                   void* stream) {
+  int rc = check_shape(B, H, N, d, scale);
+  if (rc) return rc;
+  const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
+  const Buf in[6] = {{q, tb, "q", 16},   {k, tb, "k", 16},     {v, tb, "v", 16},
+                     {o, tb, "o", 16},   {lse, lb, "lse", 4},  {dout, tb, "dout", 16}};
+  const Buf out[3] = {{dq, tb, "dq", 16}, {dk, tb, "dk", 16}, {dv, tb, "dv", 16}};
+  rc = check_bufs(in, 6, out, 3);
+  if (rc) return rc;
+  // Heads are independent and contiguous, so they run in chunks whose
+  // workspace fits the scratch array, one after another on the stream.
+  const size_t per_head = fa_bwd_workspace_bytes(1, 1, N, d);
+  if (per_head > kScratchBytes)
+    return fail(FA_ERR_UNSUPPORTED,
+                "fa_bwd_noalloc: one head of N = %d, d = %d needs %zu bytes of workspace; the scratch holds %zu",
+                N, d, per_head, kScratchBytes);
+  const int heads = B * H;
+  int chunk = (int)std::min<size_t>((size_t)heads, kScratchBytes / per_head);
+  while (chunk > 1 && fa_bwd_workspace_bytes(1, chunk, N, d) > kScratchBytes) --chunk;
+  char* ws = nullptr;
+  rc = scratch_on_current_device(&ws);
+  if (rc) return rc;
+  const size_t head_elems = (size_t)N * d;
+  for (int h0 = 0; h0 < heads; h0 += chunk) {
+    const int c = std::min(chunk, heads - h0);
+    fa::BwdArgs a{};
+    const size_t eo = (size_t)h0 * head_elems * 2;   // bytes into the bf16 tensors
+    a.q = (const char*)q + eo; a.k = (const char*)k + eo; a.v = (const char*)v + eo;
+    a.o = (const char*)o + eo; a.lse = lse + (size_t)h0 * N; a.dout = (const char*)dout + eo;
+    a.dq = (char*)dq + eo; a.dk = (char*)dk + eo; a.dv = (char*)dv + eo;
+    a.N = N; a.scale = scale; a.c = log2e_scale(scale);
+    a.H = c; a.group = 1; a.B = 1;
+    a.dq_acc = (float*)ws;
+    a.dvec = (float*)(ws + align256((size_t)c * N * d * 4));
+    rc = launched(fa::launch_bwd(fa::DType::BF16, d, causal, a, 1, c, 7, (hipStream_t)stream),
+                  "attention backward (no allocation)");
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,

@@ -212,6 +212,27 @@ FA_API int fa_bwd_det(const void* q, const void* k, const void* v, const void* o
  * sizes. */
 FA_API size_t fa_bwd_det_workspace_bytes(int B, int H, int N, int d, int causal);
 
+/* fa_bwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Same arguments
+ * (minus the workspace), checks, layouts and results as fa_bwd (bf16).
+ * The workspace is a fixed array inside the library, one per device,
+ * fa_bwd_noalloc_scratch_bytes() = 128 MiB, held while the library is
+ * loaded. The (batch, head) pairs run in chunks whose fa_bwd workspace
+ * fits it, one chunk after another on the stream, so any B and H are
+ * accepted; a single head needing more than the array
+ * (fa_bwd_workspace_bytes(1, 1, N, d) > 128 MiB, i.e. N above about
+ * 260,000 at d = 128) gives FA_ERR_UNSUPPORTED. Every call on a device
+ * shares that device's array: calls that may overlap in time on one
+ * device (different streams, or threads) race and must be serialised by
+ * the caller. The array's first use on a device looks up its address
+ * (hipGetSymbolAddress); nothing is allocated or freed. */
+FA_API int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv,
+                          int B, int H, int N, int d, float scale, int causal, void* stream);
+/* Bytes of the scratch array fa_bwd_noalloc uses (per device). */
+FA_API size_t fa_bwd_noalloc_scratch_bytes(void);
+
 /* Backward, float32 tensors ("6.1 FlashAttention V1详解", sections 6.1-6.2).
  * Same contract as fa_bwd. */
 FA_API int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,

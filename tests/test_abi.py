@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -254,3 +254,23 @@ def test_varlen_rejects_and_workspace(lib):
     assert fwd(o=cu) == _lib.FA_ERR_INVALID                        # output over cu_seqlens
     assert bwd(dq=cu) == _lib.FA_ERR_INVALID
     assert bwd(ws_bytes=1000) == _lib.FA_ERR_INVALID
+
+
+def test_noalloc_backward_rejects(lib):
+    """fa_bwd_noalloc checks its arguments before it looks up its scratch
+    array, and refuses a head whose workspace exceeds that array."""
+    assert lib.fa_bwd_noalloc_scratch_bytes() == 128 << 20
+
+    def call(N=16, d=64, B=1, H=1, scale=0.125, **over):
+        p = dict(q=A, k=A + GAP, v=A + 2 * GAP, o=A + 3 * GAP, lse=A + 4 * GAP, do=A + 5 * GAP,
+                 dq=A + 6 * GAP, dk=A + 7 * GAP, dv=A + 8 * GAP)
+        p.update(over)
+        return lib.fa_bwd_noalloc(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                                  B, H, N, d, scale, 1, None)
+    assert call(B=0) == _lib.FA_ERR_INVALID
+    assert call(d=32) == _lib.FA_ERR_UNSUPPORTED
+    assert call(q=None) == _lib.FA_ERR_INVALID
+    assert call(dq=A + 64) == _lib.FA_ERR_INVALID
+    # one head of N = 300000, d = 128 needs about 155 MB of workspace
+    assert call(N=300000, d=128) == _lib.FA_ERR_UNSUPPORTED
+    assert "scratch" in lib.fa_last_error().decode()
