@@ -280,8 +280,10 @@ def quant_fp8(x, rot=None, block_rows: int = 64, x8=None, scales=None):
     return x8, scales
 
 
-def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """O (bf16), LSE from e4m3 codes with per-64-row scales."""
+def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            block_rows: int = 64):
+    """O (bf16), LSE from e4m3 codes with per-64-row scales (block_rows = 64)
+    or one per-tensor scale broadcast in the same layout (block_rows = 0)."""
     B, H, N, d = _shape4(q8)
     nb = (N + 63) // 64
     for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
@@ -295,7 +297,7 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = 
     _check_tensor(out, "out", torch.bfloat16, (B, H, N, d))
     _check_tensor(lse, "lse", torch.float32, (B, H, N))
     st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), sq.data_ptr(), sk.data_ptr(),
-                                sv.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
+                                sv.data_ptr(), int(block_rows), out.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
                                 int(bool(causal)), _stream(q8))
     _lib.check(st, "fa_fwd_fp8")
     return out, lse

@@ -415,10 +415,14 @@ int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, float* scal
 }
 
 int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* v8, const float* sq,
-               const float* sk, const float* sv, void* o, float* lse, int B, int H, int N, int d, float scale,
-               int causal, void* stream) {
+               const float* sk, const float* sv, int block_rows, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
   int rc = check_shape(B, H, N, d, scale);
   if (rc) return rc;
+  // Both granularities fa_quant_fp8 writes share one layout (a per-tensor
+  // scale is broadcast to every 64-row entry), so the kernel reads them alike.
+  if (block_rows != 64 && block_rows != 0)
+    return fail(FA_ERR_UNSUPPORTED, "block_rows must be 64 or 0 (got %d)", block_rows);
   if (d != 128) return fail(FA_ERR_UNSUPPORTED, "fp8 forward supports d = 128 only (got %d)", d);
   const size_t n = (size_t)B * H * N * d;
   const size_t sb = (size_t)B * H * ((N + 63) / 64) * 4;

@@ -260,9 +260,13 @@ FA_API int fa_bwd_f32(const float* q, const float* k, const float* v, const floa
 FA_API int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, float* scales,
                  int B, int H, int N, int d, int block_rows, void* stream);
 
-/* Forward on fp8 inputs: q8, k8, v8 e4m3fn codes [B,H,N,d] with scales
- * sq, sk, sv [B,H,ceil(N/64)] as written by fa_quant_fp8 (the dequantised
- * value of a code is decode(code) * s of its 64-row block). Keys are taken
+/* Forward on fp8 inputs ("FlashAttention v1～v4 完整进化史", v3 part 3: both
+ * products on fp8 matrix cores, with block scales): q8, k8, v8 e4m3fn codes
+ * [B,H,N,d] with scales sq, sk, sv [B,H,ceil(N/64)] as written by
+ * fa_quant_fp8 with the same block_rows (64: one scale per 64-row block;
+ * 0: one per-tensor scale, broadcast to every entry); the dequantised value
+ * of a code is decode(code) * s of its 64-row block. Other block_rows give
+ * FA_ERR_UNSUPPORTED: the kernel's key tile is one 64-row scale block. Keys are taken
  * in tiles of 64 (one scale block each); m is the exact running maximum
  * after each tile, P~ = exp(S - m) <= 1 is rounded to e4m3 as
  * e4m3(P~ * 448) for the product with V (dequantised by sv / 448 of its
@@ -272,7 +276,7 @@ FA_API int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, floa
  * o: [B,H,N,d] bf16 (written). lse: [B,H,N] float32 (written). d must be
  * 128. */
 FA_API int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* v8,
-               const float* sq, const float* sk, const float* sv,
+               const float* sq, const float* sk, const float* sv, int block_rows,
                void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, void* stream);
 

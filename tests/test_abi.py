@@ -124,10 +124,15 @@ def test_fp8_rejects(lib):
     assert lib.fa_quant_fp8(q, None, None, A + 2 * GAP, 1, 1, 64, 128, 64, None) == _lib.FA_ERR_INVALID
     assert lib.fa_quant_fp8(q, None, A + 256, A + 2 * GAP, 1, 1, 64, 128, 64, None) == _lib.FA_ERR_INVALID
     s = A + 3 * GAP
-    assert lib.fa_fwd_fp8(A, A + GAP, A + 2 * GAP, s, s + GAP, s + 2 * GAP, s + 3 * GAP, s + 4 * GAP,
+    assert lib.fa_fwd_fp8(A, A + GAP, A + 2 * GAP, s, s + GAP, s + 2 * GAP, 64, s + 3 * GAP, s + 4 * GAP,
                           1, 1, 64, 64, 0.125, 0, None) == _lib.FA_ERR_UNSUPPORTED
-    assert lib.fa_fwd_fp8(A, A + GAP, A + 2 * GAP, s, s + GAP, s + 2 * GAP, A + 256, s + 4 * GAP,
+    assert lib.fa_fwd_fp8(A, A + GAP, A + 2 * GAP, s, s + GAP, s + 2 * GAP, 64, A + 256, s + 4 * GAP,
                           1, 1, 64, 128, 0.125, 0, None) == _lib.FA_ERR_INVALID
+    # scale blocks other than 64 rows (or one per tensor) are not supported
+    for br in (32, 128, -1):
+        assert lib.fa_fwd_fp8(A, A + GAP, A + 2 * GAP, s, s + GAP, s + 2 * GAP, br, s + 3 * GAP, s + 4 * GAP,
+                              1, 1, 64, 128, 0.125, 0, None) == _lib.FA_ERR_UNSUPPORTED
+        assert "block_rows" in lib.fa_last_error().decode()
 
 
 def test_det_workspace_is_linear_in_n(lib):

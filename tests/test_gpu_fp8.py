@@ -239,7 +239,7 @@ def workload5(fa):
         k8, sk = fa.quant_fp8(dev["k"], rot=rot if use_rot else None, block_rows=br)
         v8, sv = fa.quant_fp8(dev["v"], block_rows=br)
         announce(f"workload 5: fa_fwd_fp8 ({name})")
-        o, lse = fa.fwd_fp8(q8, k8, v8, sq, sk, sv, causal=False, scale=w.scale)
+        o, lse = fa.fwd_fp8(q8, k8, v8, sq, sk, sv, causal=False, scale=w.scale, block_rows=br)
         _sync()
         out[name] = (o.float().cpu().numpy(), lse.cpu().numpy(), (q8, sq, k8, sk, v8, sv))
     del dev
