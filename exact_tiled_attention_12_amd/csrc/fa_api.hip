@@ -142,12 +142,9 @@ int bwd_common(fa::DType dt, const void* q, const void* k, const void* v, const 
   a.dq_acc = (float*)ws;
   a.dvec = (float*)((char*)ws + align256((size_t)B * H * N * d * 4));
   if (det) {
-    // fixed order: for d = 64 a second dQ accumulator (one per key half),
-    // then D, then the per-query-tile counters and the error flag
+    // fixed order: the per-query-tile counters and the error flag after D
     const size_t n_cnt = (size_t)B * H * fa::bwd_row_tiles(N) * fa::kBwdSlots;
-    const size_t acc = align256((size_t)B * H * N * 128 * 4);
-    a.dvec = (float*)((char*)ws + acc);
-    a.dq_cnt = (int*)((char*)ws + acc + align256((size_t)B * H * N * 4));
+    a.dq_cnt = (int*)((char*)ws + fa_bwd_workspace_bytes(B, H, N, d));
     a.dq_err = a.dq_cnt + n_cnt;
     a.n_cnt = (int)(n_cnt + 1);
   } else if (H_kv < H) {
@@ -238,13 +235,10 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
 
 size_t fa_bwd_det_workspace_bytes(int B, int H, int N, int d, int causal) {
   (void)causal;   // the same for both masks
-  if (fa_bwd_workspace_bytes(B, H, N, d) == 0) return 0;
-  // float32 dQ accumulators (d = 128: one; d = 64: one per key half, B H N
-  // 64 floats each), D, then kBwdSlots counters per (batch, head, 32-row
-  // query tile) and the error flag
-  const size_t bhn = (size_t)B * H * N;
-  return align256(bhn * 128 * 4) + align256(bhn * 4) +
-         align256(((size_t)B * H * fa::bwd_row_tiles(N) * fa::kBwdSlots + 1) * 4);
+  const size_t base = fa_bwd_workspace_bytes(B, H, N, d);
+  if (base == 0) return 0;
+  // counters: kBwdSlots per (batch, head, 32-row query tile), then the error flag
+  return base + align256(((size_t)B * H * fa::bwd_row_tiles(N) * fa::kBwdSlots + 1) * 4);
 }
 
 int fa_bwd_det(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -85,11 +85,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a, long long 
     float* acc = a.dq_acc + off;
 #pragma unroll
     for (int e = 0; e < E; e += 4) *(f32x4*)(acc + e) = f32x4{0.f, 0.f, 0.f, 0.f};
-    // fixed order, d = 64: the second key half's accumulator
-    if (D == 64 && a.dq_cnt != nullptr) {
-#pragma unroll
-      for (int e = 0; e < E; e += 4) *(f32x4*)(acc + rows * D + e) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
   }
   // Fixed-order mode: clear the per-tile counters and the error flag.
   if (a.dq_cnt != nullptr && gid < a.n_cnt) a.dq_cnt[gid] = 0;
@@ -105,10 +100,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, long long n
   using T = typename Tr::T;
   const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n4) return;
-  f32x4 acc = *(const f32x4*)(a.dq_acc + 4 * i);
-  // fixed order, d = 64: key half 0's accumulator plus key half 1's
-  if (D == 64 && a.dq_cnt != nullptr) acc += *(const f32x4*)(a.dq_acc + 4 * (i + n4));
-  f32x4 v = acc * a.scale;
+  f32x4 v = *(const f32x4*)(a.dq_acc + 4 * i) * a.scale;
   // Fixed-order mode: a wait that ran out left the order (and maybe the
   // sum) unknown; dq becomes NaN so that the failure cannot pass unseen.
   if (a.dq_err != nullptr && *(const volatile int*)a.dq_err != 0) v = f32x4{NAN, NAN, NAN, NAN};

@@ -45,6 +45,8 @@
 //     between them;
 //   * rows of the LDS tiles are XOR-swizzled per 16-byte chunk so that both
 //     the 16-row reads and the 4-row transposed reads hit distinct banks.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -66,6 +68,9 @@ constexpr unsigned kSpinLimit = 1u << 20;
 
 #define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
+template <int N>
+using IC = std::integral_constant<int, N>;
+
 template <int D>
 struct Cfg {
   static constexpr int RB = 2 * D;                   // bytes per row
@@ -81,7 +86,7 @@ struct Cfg {
   static constexpr int R_LOADS = 2 * QT_LOADS + 1;   // copies per wave per query tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
-  static constexpr int NQ = D == 128 ? 16 : 8;       // dQ products per wave per tile
+  static constexpr int NQ = 16;                      // dQ products per dQ-forming wave per tile
   static constexpr int LDS_BYTES = K_BYTES + 2 * DS_BYTES + kStages * STAGE;
   static_assert(QT_LOADS >= 1 && K_LOADS >= 1, "tile split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -220,10 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   const int qt_begin = CAUSAL ? k0 / kBR : 0;
   const int nt = n_qt - qt_begin;   // query tiles visited per query head (>= 1)
   const int nvis = nt;              // visits: query tile n_qt - 1 - i at visit i
-  // (Fixed order, d = 64: each key half has an accumulator of its own, the
-  // second one B H N d floats after the first; the finish pass adds them.)
-  const size_t dq_half = DET && D == 64 && wave >= 2 ? (size_t)a.B * a.H * (size_t)N * D : 0;
-  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(a.dq_acc + dq_half + qbase, (unsigned)N * D * 4);
+  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(a.dq_acc + qbase, (unsigned)N * D * 4);
   const unsigned kt_a = (unsigned)(uintptr_t)LDS(unsigned char, kt_s);
   const unsigned rg_a = (unsigned)(uintptr_t)LDS(unsigned char, rg_s);
 
@@ -297,9 +299,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
                    8 * (tq & 1);
   const unsigned w_lane = (unsigned)(wave * kKW + l32) * 64;   // dS^T write row base
   const int wsw = (l32 >> 2) & 3;
-  // dQ slice of this wave: column block db_q over keys [kc_q0, kc_q0 + NQ) x 16.
+  // dQ slice of this wave: column block db_q over all 256 keys (NQ steps of
+  // 16). For d = 64 waves 0 and 1 form the two column blocks and waves 2
+  // and 3 form none (their dQ atomics are no-ops): every dQ element then
+  // gets one add per key tile; splitting the keys over two waves per block
+  // instead doubles the atomic traffic, which bounds the d = 64 kernel.
   const int db_q = D == 128 ? wave : (wave & 1);
-  const int kc_q0 = D == 128 ? 0 : (wave >> 1) * 8;
+  constexpr int kc_q0 = 0;
+  const bool dq_wave = D == 128 || wave < 2;
 
   f32x16 dk[2][C::DBLK], dv[2][C::DBLK];
 #pragma unroll
@@ -339,9 +346,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   };
 
   // ---- fixed-order dQ (DET). Each wave adds to elements no other wave of
-  // the workgroup touches (d = 128: its column block; d = 64: its column
-  // block of its key half's accumulator), so each has a counter (slot) of
-  // its own per query tile and waits only on the same wave of lower key
+  // the workgroup touches (its column block; for d = 64 waves 2 and 3 add
+  // nothing and keep their counters in step), so each has a counter (slot)
+  // of its own per query tile and waits only on the same wave of lower key
   // tiles: key tile kt's add to a query tile is the kt-th one there.
   const int dq_turn = kt;
   // A device-coherent read of the counter of the tile of `visit` (sc1: the
@@ -448,161 +455,310 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
       lim[kb] = !mask ? -1 : (!active || key >= N) ? kBR : CAUSAL ? key - q0 : -1;
     }
 
-    // L and D of the tile's rows (each lane reads those of its row slots).
-    const float* Ls = (const float*)(qs + 2 * C::QT);
-    const float* Ds = (const float*)(qs + 2 * C::QT + C::LD);
-    // Softmax of row slot r of key block kb: P = exp2(S c - L log2 e), dS =
-    // P (dP - D). Entry (q0 + ql, key) is kept iff ql >= lim.
-    f32x16 s[2], dp[2];
-    bf16x8 pf[2][2], df[2][2];
-    constexpr int SPK = 16 / C::KSTEPS;   // softmax evaluations per d step (= per dV/dK step)
-    static_assert(SPK == 16 / (2 * C::DBLK), "one evaluation count per step");
-    // L (times log2 e) and D of the row slots r0 .. r0+SPK-1, read from LDS one
-    // step before their use, ahead of that step's operand reads: waiting for
-    // them then never waits for the operands of the step after.
-    struct LDv {
-      float l[SPK], d[SPK];
-    };
-    auto rd_ld = [&](int r0) INL {
-      LDv v;
+    // ---- d = 64: both key blocks in one pass (the visit is bound by its
+    // LDS reads and round trips, not by the matrix cores): phase A forms S
+    // and dP of both blocks one d step at a time, so every Q and dO
+    // fragment feeds two products; phase B runs the softmax of both blocks
+    // beside the dQ products of visit i-1; phase C writes dS^T and forms
+    // dV and dK of both blocks, each transposed operand read once for both,
+    // with the dQ atomics of visit i-1 spread over its steps.
+    if constexpr (D == 64) {
+      // L and D of row slot r = query slot_key(r, hh): slots 4 q .. 4 q + 3
+      // are 4 consecutive rows, one 16-byte read each.
+      const float* Ls = (const float*)(qs + 2 * C::QT);
+      const float* Ds = (const float*)(qs + 2 * C::QT + C::LD);
+      struct LD4 {
+        float l[4], d[4];   // L log2 e and D of 4 row slots
+      };
+      auto rd_ld4 = [&](int q) INL {
+        LD4 v;
+        const int o = 16 * (q >> 1) + 8 * hh + 4 * (q & 1);
+        const f32x4 l0 = *LDS(const f32x4, Ls + o), d0 = *LDS(const f32x4, Ds + o);
 #pragma unroll
-      for (int t = 0; t < SPK; ++t) {
-        const int ql = slot_key(r0 + t, hh);
-        v.l[t] = *LDS(const float, Ls + ql);
-        v.d[t] = *LDS(const float, Ds + ql);
+        for (int t = 0; t < 4; ++t) {
+          v.l[t] = l0[t] * kLog2e;
+          v.d[t] = d0[t];
+        }
+        return v;
+      };
+      f32x16 s[2], dp[2];
+      bf16x8 pf[2][2], df[2][2];
+      auto soft = [&](int kb, int r, float l2, float dd) INL {
+        const int ql = slot_key(r, hh);
+        float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -l2));
+        p = ql >= lim[kb] ? p : 0.f;
+        const float ds = p * (dp[kb][r] - dd);
+        pf[kb][r >> 3][r & 7] = (__bf16)p;
+        df[kb][r >> 3][r & 7] = (__bf16)ds;
+      };
+      // Phase A.
+      bf16x8 fq[2], fg[2], fk0[2], fk1[2];
+      auto rd_a = [&](int kk) INL {
+        const int b = kk % 2;
+        fq[b] = *LDS(bf16x8, qs + (a_lane ^ (32u * kk)));
+        fg[b] = *LDS(bf16x8, qs + C::QT + (a_lane ^ (32u * kk)));
+        fk0[b] = *LDS(bf16x8, kt_s + (k_lane ^ (32u * kk)));
+        fk1[b] = *LDS(bf16x8, kt_s + (k_lane ^ (32u * kk)) + 32 * C::RB);
+      };
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
       }
-      return v;
-    };
-    auto soft = [&](int kb, int r, const LDv& ld) INL {
-      const int ql = slot_key(r, hh);
-      const float l2 = ld.l[r % SPK] * kLog2e, dd = ld.d[r % SPK];
-      float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -l2));
-      p = ql >= lim[kb] ? p : 0.f;
-      const float ds = p * (dp[kb][r] - dd);
-      pf[kb][r >> 3][r & 7] = (__bf16)p;
-      df[kb][r >> 3][r & 7] = (__bf16)ds;
-    };
-
-    // ---- Phase 1: S and dP of tile i for key block 0, then for key block 1
-    // beside the softmax of block 0 (two evaluations per d step); operands
-    // read one step ahead.
-    bf16x8 fq[2], fg[2], fk[2];
-    LDv ldv[2];
-    auto rd_sdp = [&](int kb, int kk) INL {
-      const int b = kk % 2;
-      fq[b] = *LDS(bf16x8, qs + (a_lane ^ (32u * kk)));
-      fg[b] = *LDS(bf16x8, qs + C::QT + (a_lane ^ (32u * kk)));
-      fk[b] = *LDS(bf16x8, kt_s + (k_lane ^ (32u * kk)) + kb * 32 * C::RB);
-    };
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // Copies of visit i+2 go to the stage of visit i-1 (free since the
-      // barrier). Issued here rather than right after the barrier, where
-      // they would queue behind the previous visit's dQ atomics and stall.
-      if (kb == 1) issue_qtile(i + 2);
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-      if (kb == 1) ldv[0] = rd_ld(0);
-      rd_sdp(kb, 0);
+      rd_a(0);
 #pragma unroll
       for (int kk = 0; kk < C::KSTEPS; ++kk) {
         const int b = kk % 2;
-        if (kk + 1 < C::KSTEPS) {
-          if (kb == 1) ldv[(kk + 1) % 2] = rd_ld((kk + 1) * SPK);
-          rd_sdp(kb, kk + 1);
-        }
+        if (kk + 1 < C::KSTEPS) rd_a(kk + 1);
+        // Copies of visit i+2 go to the stage of visit i-1 (free since the
+        // barrier); issued here rather than right after the barrier, where
+        // they would queue behind the previous visit's dQ atomics and stall.
+        if (kk == C::KSTEPS / 2) issue_qtile(i + 2);
         __builtin_amdgcn_sched_barrier(0);
-        s[kb] = mma(fq[b], fk[b], s[kb]);
-        dp[kb] = mma(fg[b], vf[kb][kk], dp[kb]);
-        if (kb == 1) {
-#pragma unroll
-          for (int t = 0; t < SPK; ++t) soft(0, kk * SPK + t, ldv[b]);
-        }
+        s[0] = mma(fq[b], fk0[b], s[0]);
+        dp[0] = mma(fg[b], vf[0][kk], dp[0]);
+        s[1] = mma(fq[b], fk1[b], s[1]);
+        dp[1] = mma(fg[b], vf[1][kk], dp[1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
-
-    // ---- Phase 2: dV += P^T dO and dK += dS^T Q of key block 0 beside the
-    // softmax of key block 1; phase 3: the same products of key block 1 with
-    // dQ of visit i-1 (its dS^T is complete in LDS) interleaved. The B operands
-    // of dV and dK are read transposed from the ring one (ks, db) step ahead
-    // (once per key block); the dQ operands one product ahead.
-    auto trd = [&](int step) INL {
-      const int ks = step / C::DBLK, db = step % C::DBLK;
-      const unsigned char* ko = qs + ks * 16 * C::RB;
-      Tr4 t;
-      t.v[0] = tr_read(ko + C::QT + (t_lane[0] ^ (64u * db)));
-      t.v[1] = tr_read(ko + C::QT + (t_lane[1] ^ (64u * db)));
-      t.v[2] = tr_read(ko + (t_lane[0] ^ (64u * db)));
-      t.v[3] = tr_read(ko + (t_lane[1] ^ (64u * db)));
-      return t;
-    };
-    constexpr int NS = 2 * C::DBLK;   // (ks, db) steps per key block
-    auto dvdk = [&](int kb, const Tr4& t, int step) INL {
-      const int ks = step / C::DBLK, db = step % C::DBLK;
-      dv[kb][db] = mma(pf[kb][ks], join(t.v[0], t.v[1]), dv[kb][db]);
-      dk[kb][db] = mma(df[kb][ks], join(t.v[2], t.v[3]), dk[kb][db]);
-    };
-    Tr4 top[2];
-    ldv[0] = rd_ld(0);
-    top[0] = trd(0);
-    constexpr int SPS = SPK;          // softmax evaluations per step
+      // Phase B: an equal share of the 32 evaluations per dQ product; dQ
+      // operands one product ahead, L and D one quarter of the slots ahead.
+      // Waves that form no dQ run the evaluations alone.
+      constexpr int EPM = 32 / C::NQ;
+      static_assert(EPM * C::NQ == 32 && C::NQ % 4 == 0, "evaluation split");
+      constexpr int MQ = C::NQ / 4;   // products per quarter of the slots
+      f32x16 dq_acc = f32x16{};
+      auto phase_b = [&](auto with_dq) INL {
+        constexpr bool WQ = decltype(with_dq)::value != 0;
+        LD4 ldq[2];
+        ldq[0] = rd_ld4(0);
+        Tr4 qop[2];
+        if constexpr (WQ) qop[0] = rd_dq(sb_prev, 0);
 #pragma unroll
-    for (int step = 0; step < NS; ++step) {
-      const int b = step % 2;
-      if (step + 1 < NS) {
-        ldv[(step + 1) % 2] = rd_ld((step + 1) * SPS);
-        top[(step + 1) % 2] = trd(step + 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      dvdk(0, top[b], step);
+        for (int m = 0; m < C::NQ; ++m) {
+          if constexpr (WQ) {
+            if (m + 1 < C::NQ) qop[(m + 1) % 2] = rd_dq(sb_prev, m + 1);
+          }
+          if (m % MQ == 0 && m / MQ + 1 < 4) ldq[(m / MQ + 1) % 2] = rd_ld4(m / MQ + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (WQ)
+            dq_acc = mma(join(qop[m % 2].v[0], qop[m % 2].v[1]), join(qop[m % 2].v[2], qop[m % 2].v[3]), dq_acc);
 #pragma unroll
-      for (int t = 0; t < SPS; ++t) soft(1, step * SPS + t, ldv[b]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    {
-      // dS^T rows (keys) of this wave: 8 queries per 16-byte write.
-      unsigned char* sp = dsb(i & 1) + w_lane;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) *LDS(bf16x8, sp + kb * 32 * 64 + 16 * ((2 * k2 + hh) ^ wsw)) = df[kb][k2];
-    }
-    top[0] = trd(0);
-    Tr4 qop[2];
-    qop[0] = rd_dq(sb_prev, 0);
-    f32x16 dq_acc = f32x16{};
-    // dQ products in the first quarter of the steps, its atomics spread over
-    // the rest (one burst of 16 would stall on vector-memory issue).
-    constexpr int QS = NS / 4;                 // steps that carry dQ products
-    constexpr int QPS = C::NQ / QS;            // dQ products per such step
-#pragma unroll
-    for (int step = 0; step < NS; ++step) {
-      const int b = step % 2;
-      if (step + 1 < NS) top[(step + 1) % 2] = trd(step + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      dvdk(1, top[b], step);
-      if (step < QS) {
-#pragma unroll
-        for (int t = 0; t < QPS; ++t) {
-          const int m = step * QPS + t;
-          if (m + 1 < C::NQ) qop[(m + 1) % 2] = rd_dq(sb_prev, m + 1);
-          dq_acc = mma(join(qop[m % 2].v[0], qop[m % 2].v[1]), join(qop[m % 2].v[2], qop[m % 2].v[3]), dq_acc);
+          for (int t = 0; t < EPM; ++t) {
+            const int e = m * EPM + t, r = e >> 1, kb = e & 1;
+            soft(kb, r, ldq[(r >> 2) % 2].l[r & 3], ldq[(r >> 2) % 2].d[r & 3]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-      } else {
+      };
+      if (dq_wave)
+        phase_b(IC<1>{});
+      else
+        phase_b(IC<0>{});
+      // Phase C.
+      {
+        // dS^T rows (keys) of this wave: 8 queries per 16-byte write.
+        unsigned char* sp = dsb(i & 1) + w_lane;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) *LDS(bf16x8, sp + kb * 32 * 64 + 16 * ((2 * k2 + hh) ^ wsw)) = df[kb][k2];
+      }
+      auto trd = [&](int step) INL {
+        const int ks = step / C::DBLK, db = step % C::DBLK;
+        const unsigned char* ko = qs + ks * 16 * C::RB;
+        Tr4 t;
+        t.v[0] = tr_read(ko + C::QT + (t_lane[0] ^ (64u * db)));
+        t.v[1] = tr_read(ko + C::QT + (t_lane[1] ^ (64u * db)));
+        t.v[2] = tr_read(ko + (t_lane[0] ^ (64u * db)));
+        t.v[3] = tr_read(ko + (t_lane[1] ^ (64u * db)));
+        return t;
+      };
+      constexpr int NS = 2 * C::DBLK;   // (ks, db) steps
+      auto dvdk = [&](int kb, const Tr4& t, int step) INL {
+        const int ks = step / C::DBLK, db = step % C::DBLK;
+        dv[kb][db] = mma(pf[kb][ks], join(t.v[0], t.v[1]), dv[kb][db]);
+        dk[kb][db] = mma(df[kb][ks], join(t.v[2], t.v[3]), dk[kb][db]);
+      };
+      Tr4 top[2];
+      top[0] = trd(0);
+#pragma unroll
+      for (int step = 0; step < NS; ++step) {
+        const int b = step % 2;
+        if (step + 1 < NS) top[(step + 1) % 2] = trd(step + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dvdk(0, top[b], step);
+        dvdk(1, top[b], step);
         // Fixed order: read the counter of this visit's own tile now (the
         // next visit adds to it); its value is needed only after the next
         // barrier, so the read costs no wait.
         if constexpr (DET) {
-          if (step == QS) dq_seen = dq_peek(i);
+          if (step == 0) dq_seen = dq_peek(i);
         }
-        // memory operations r in [lo, hi) of the NDQ, split evenly over steps QS .. NS-1
-        constexpr int NA = NS - QS;
-        const int lo = (step - QS) * NDQ / NA, hi = (step - QS + 1) * NDQ / NA;
+        // dQ memory operations r in [lo, hi) of the NDQ, split evenly over the steps
+        const int lo = step * NDQ / NS, hi = (step + 1) * NDQ / NS;
 #pragma unroll
-        for (int r = lo; r < hi; ++r) dq_atomic(dq_acc, i - 1, i > 0, r);
+        for (int r = lo; r < hi; ++r) dq_atomic(dq_acc, i - 1, i > 0 && dq_wave, r);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      // L and D of the tile's rows (each lane reads those of its row slots).
+      const float* Ls = (const float*)(qs + 2 * C::QT);
+      const float* Ds = (const float*)(qs + 2 * C::QT + C::LD);
+      // Softmax of row slot r of key block kb: P = exp2(S c - L log2 e), dS =
+      // P (dP - D). Entry (q0 + ql, key) is kept iff ql >= lim.
+      f32x16 s[2], dp[2];
+      bf16x8 pf[2][2], df[2][2];
+      constexpr int SPK = 16 / C::KSTEPS;   // softmax evaluations per d step (= per dV/dK step)
+      static_assert(SPK == 16 / (2 * C::DBLK), "one evaluation count per step");
+      // L (times log2 e) and D of the row slots r0 .. r0+SPK-1, read from LDS one
+      // step before their use, ahead of that step's operand reads: waiting for
+      // them then never waits for the operands of the step after.
+      struct LDv {
+        float l[SPK], d[SPK];
+      };
+      auto rd_ld = [&](int r0) INL {
+        LDv v;
+  #pragma unroll
+        for (int t = 0; t < SPK; ++t) {
+          const int ql = slot_key(r0 + t, hh);
+          v.l[t] = *LDS(const float, Ls + ql);
+          v.d[t] = *LDS(const float, Ds + ql);
+        }
+        return v;
+      };
+      auto soft = [&](int kb, int r, const LDv& ld) INL {
+        const int ql = slot_key(r, hh);
+        const float l2 = ld.l[r % SPK] * kLog2e, dd = ld.d[r % SPK];
+        float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -l2));
+        p = ql >= lim[kb] ? p : 0.f;
+        const float ds = p * (dp[kb][r] - dd);
+        pf[kb][r >> 3][r & 7] = (__bf16)p;
+        df[kb][r >> 3][r & 7] = (__bf16)ds;
+      };
+
+      // ---- Phase 1: S and dP of tile i for key block 0, then for key block 1
+      // beside the softmax of block 0 (two evaluations per d step); operands
+      // read one step ahead.
+      bf16x8 fq[2], fg[2], fk[2];
+      LDv ldv[2];
+      auto rd_sdp = [&](int kb, int kk) INL {
+        const int b = kk % 2;
+        fq[b] = *LDS(bf16x8, qs + (a_lane ^ (32u * kk)));
+        fg[b] = *LDS(bf16x8, qs + C::QT + (a_lane ^ (32u * kk)));
+        fk[b] = *LDS(bf16x8, kt_s + (k_lane ^ (32u * kk)) + kb * 32 * C::RB);
+      };
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // Copies of visit i+2 go to the stage of visit i-1 (free since the
+        // barrier). Issued here rather than right after the barrier, where
+        // they would queue behind the previous visit's dQ atomics and stall.
+        if (kb == 1) issue_qtile(i + 2);
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+        if (kb == 1) ldv[0] = rd_ld(0);
+        rd_sdp(kb, 0);
+  #pragma unroll
+        for (int kk = 0; kk < C::KSTEPS; ++kk) {
+          const int b = kk % 2;
+          if (kk + 1 < C::KSTEPS) {
+            if (kb == 1) ldv[(kk + 1) % 2] = rd_ld((kk + 1) * SPK);
+            rd_sdp(kb, kk + 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          s[kb] = mma(fq[b], fk[b], s[kb]);
+          dp[kb] = mma(fg[b], vf[kb][kk], dp[kb]);
+          if (kb == 1) {
+  #pragma unroll
+            for (int t = 0; t < SPK; ++t) soft(0, kk * SPK + t, ldv[b]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ---- Phase 2: dV += P^T dO and dK += dS^T Q of key block 0 beside the
+      // softmax of key block 1; phase 3: the same products of key block 1 with
+      // dQ of visit i-1 (its dS^T is complete in LDS) interleaved. The B operands
+      // of dV and dK are read transposed from the ring one (ks, db) step ahead
+      // (once per key block); the dQ operands one product ahead.
+      auto trd = [&](int step) INL {
+        const int ks = step / C::DBLK, db = step % C::DBLK;
+        const unsigned char* ko = qs + ks * 16 * C::RB;
+        Tr4 t;
+        t.v[0] = tr_read(ko + C::QT + (t_lane[0] ^ (64u * db)));
+        t.v[1] = tr_read(ko + C::QT + (t_lane[1] ^ (64u * db)));
+        t.v[2] = tr_read(ko + (t_lane[0] ^ (64u * db)));
+        t.v[3] = tr_read(ko + (t_lane[1] ^ (64u * db)));
+        return t;
+      };
+      constexpr int NS = 2 * C::DBLK;   // (ks, db) steps per key block
+      auto dvdk = [&](int kb, const Tr4& t, int step) INL {
+        const int ks = step / C::DBLK, db = step % C::DBLK;
+        dv[kb][db] = mma(pf[kb][ks], join(t.v[0], t.v[1]), dv[kb][db]);
+        dk[kb][db] = mma(df[kb][ks], join(t.v[2], t.v[3]), dk[kb][db]);
+      };
+      Tr4 top[2];
+      ldv[0] = rd_ld(0);
+      top[0] = trd(0);
+      constexpr int SPS = SPK;          // softmax evaluations per step
+  #pragma unroll
+      for (int step = 0; step < NS; ++step) {
+        const int b = step % 2;
+        if (step + 1 < NS) {
+          ldv[(step + 1) % 2] = rd_ld((step + 1) * SPS);
+          top[(step + 1) % 2] = trd(step + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dvdk(0, top[b], step);
+  #pragma unroll
+        for (int t = 0; t < SPS; ++t) soft(1, step * SPS + t, ldv[b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        // dS^T rows (keys) of this wave: 8 queries per 16-byte write.
+        unsigned char* sp = dsb(i & 1) + w_lane;
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) *LDS(bf16x8, sp + kb * 32 * 64 + 16 * ((2 * k2 + hh) ^ wsw)) = df[kb][k2];
+      }
+      top[0] = trd(0);
+      Tr4 qop[2];
+      qop[0] = rd_dq(sb_prev, 0);
+      f32x16 dq_acc = f32x16{};
+      // dQ products in the first quarter of the steps, its atomics spread over
+      // the rest (one burst of 16 would stall on vector-memory issue).
+      constexpr int QS = NS / 4;                 // steps that carry dQ products
+      constexpr int QPS = C::NQ / QS;            // dQ products per such step
+  #pragma unroll
+      for (int step = 0; step < NS; ++step) {
+        const int b = step % 2;
+        if (step + 1 < NS) top[(step + 1) % 2] = trd(step + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dvdk(1, top[b], step);
+        if (step < QS) {
+  #pragma unroll
+          for (int t = 0; t < QPS; ++t) {
+            const int m = step * QPS + t;
+            if (m + 1 < C::NQ) qop[(m + 1) % 2] = rd_dq(sb_prev, m + 1);
+            dq_acc = mma(join(qop[m % 2].v[0], qop[m % 2].v[1]), join(qop[m % 2].v[2], qop[m % 2].v[3]), dq_acc);
+          }
+        } else {
+          // Fixed order: read the counter of this visit's own tile now (the
+          // next visit adds to it); its value is needed only after the next
+          // barrier, so the read costs no wait.
+          if constexpr (DET) {
+            if (step == QS) dq_seen = dq_peek(i);
+          }
+          // memory operations r in [lo, hi) of the NDQ, split evenly over steps QS .. NS-1
+          constexpr int NA = NS - QS;
+          const int lo = (step - QS) * NDQ / NA, hi = (step - QS + 1) * NDQ / NA;
+  #pragma unroll
+          for (int r = lo; r < hi; ++r) dq_atomic(dq_acc, i - 1, i > 0, r);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
     }
   }
 
@@ -618,17 +774,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   {
     const unsigned char* sb = dsb((nvis - 1) & 1);
     Tr4 qop[3];
-    qop[0] = rd_dq(sb, 0);
-    qop[1] = rd_dq(sb, 1);
     f32x16 dq_acc = f32x16{};
+    if (dq_wave) {
+      qop[0] = rd_dq(sb, 0);
+      qop[1] = rd_dq(sb, 1);
 #pragma unroll
-    for (int m = 0; m < C::NQ; ++m) {
-      if (m + 2 < C::NQ) qop[(m + 2) % 3] = rd_dq(sb, m + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      dq_acc = mma(join(qop[m % 3].v[0], qop[m % 3].v[1]), join(qop[m % 3].v[2], qop[m % 3].v[3]), dq_acc);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int m = 0; m < C::NQ; ++m) {
+        if (m + 2 < C::NQ) qop[(m + 2) % 3] = rd_dq(sb, m + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        dq_acc = mma(join(qop[m % 3].v[0], qop[m % 3].v[1]), join(qop[m % 3].v[2], qop[m % 3].v[3]), dq_acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    dq_atomics(dq_acc, nvis - 1, true);
+    dq_atomics(dq_acc, nvis - 1, dq_wave);
     if constexpr (DET) {
       __builtin_amdgcn_s_waitcnt(wait_vm(0));
       if (nvis >= 2) dq_release(nvis - 2);

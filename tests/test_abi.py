@@ -137,19 +137,17 @@ def test_fp8_rejects(lib):
 
 def test_det_workspace_is_linear_in_n(lib):
     """The fixed-order backward keeps the method's O(N) extra memory ("6.1
-    FlashAttention V1详解", 6.3): float32 dQ accumulators (d = 128: one,
-    which is the plain backward's workspace with D; d = 64: one per key half)
-    and D, plus 4 int32 counters per 32-row query tile and an error flag; the
-    same for both masks."""
+    FlashAttention V1详解", 6.3): the plain backward's workspace (the float32
+    dQ accumulator and D), plus 4 int32 counters per 32-row query tile and an
+    error flag; the same for both masks."""
     def al(x):
         return (x + 255) // 256 * 256
     for (B, H, N, d, causal) in [(1, 1, 1, 64, 0), (1, 1, 1, 64, 1), (2, 3, 1000, 128, 1), (2, 3, 1000, 64, 0),
                                  (1, 2, 257, 128, 1), (1, 32, 16384, 128, 1), (1, 32, 16384, 128, 0)]:
         got = lib.fa_bwd_det_workspace_bytes(B, H, N, d, causal)
         counters = al(4 * (B * H * (-(-N // 32)) * 4 + 1))
-        assert got == al(4 * B * H * N * 128) + al(4 * B * H * N) + counters, (B, H, N, d, causal)
-        if d == 128:
-            assert got == lib.fa_bwd_workspace_bytes(B, H, N, d) + counters
+        assert got == al(4 * B * H * N * d) + al(4 * B * H * N) + counters, (B, H, N, d, causal)
+        assert got == lib.fa_bwd_workspace_bytes(B, H, N, d) + counters
     # linear in N: doubling N (a multiple of 32) doubles every part but the flag
     for N in (1024, 4096, 16384):
         one, two = (lib.fa_bwd_det_workspace_bytes(1, 32, n, 128, 1) for n in (N, 2 * N))
