@@ -16,11 +16,19 @@ Sources:
     finite magnitude is 448. Encoding rounds to nearest, ties to even, after
     saturating magnitudes above 448 to 448.
   * Block granularity is not stated. Reading: one scale per 64 consecutive
-    rows (all d columns) of one (batch, head); s = amax / 448 (s = 1 when the
-    block is all zero). Per-tensor baseline: one s for the whole tensor.
+    rows (all d columns) of one (batch, head). Per-tensor baseline: one s
+    for the whole tensor.
+  * The form of a block's scale is not stated either. Reading: s is the
+    smallest power of two at or above amax / 448 (amax / 448 first rounded
+    to float32), kept at or above 2^-126; s = 1 when the block is all zero.
+    A power of two divides exactly (the only rounding is the e4m3 one), the
+    block's largest element lands in (224, 448], and it is the form the fp8
+    matrix cores accept as a block scale (an 8-bit exponent), so the product
+    with V can be scaled block by block without touching the accumulator.
   * Where a float decides a code (the division x / s), it is taken in
-    float32, the precision the GPU quantiser uses; s itself is
-    float32(amax) / 448 rounded to float32.
+    float32, the precision the GPU quantiser uses; s is derived from
+    float32(amax) / 448 rounded to float32 (and x / s is exact, s being a
+    power of two).
 
 Pins: tests/test_oracle_fp8.py (all 65,536 bf16 bit patterns against the
 CPU library cast to float8_e4m3fn, hand-decoded codes, scale properties).
@@ -34,7 +42,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "block_scales",
+__all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "pow2_scale", "block_scales",
            "quantize", "dequantize", "fp8_attention_tiled"]
 
 E4M3_MAX = 448.0
@@ -92,30 +100,38 @@ def e4m3_encode(x) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def block_scales(x, block_rows: int) -> np.ndarray:
-    """Scales s = amax / 448 in float32 for x of shape [B, H, N, d].
+def pow2_scale(r) -> np.ndarray:
+    """Smallest power of two at or above r (r >= 0, float32 values), at least
+    2^-126; 1 where r == 0. Returned as float32 (exact)."""
+    r = np.asarray(r, dtype=np.float64)
+    m, e = np.frexp(np.where(r > 0, r, 1.0))       # r = m 2^e, 0.5 <= m < 1
+    s = np.where(m == 0.5, np.ldexp(1.0, e - 1), np.ldexp(1.0, e))
+    s = np.maximum(s, 2.0 ** -126)
+    return np.where(r > 0, s, 1.0).astype(np.float32)
 
+
+def block_scales(x, block_rows: int) -> np.ndarray:
+    """Block scales in float32 for x of shape [B, H, N, d].
+
+    s = the smallest power of two at or above float32(amax) / 448 (rounded to
+    float32), at least 2^-126; s = 1 for an all-zero block.
     block_rows > 0: one scale per block of ``block_rows`` rows of each
     (batch, head), shape [B, H, ceil(N / block_rows)]. block_rows == 0: one
     scale for the whole tensor, returned broadcast to shape [B, H, ceil(N/64)].
-    An all-zero block gets s = 1.
     """
     x = np.asarray(x, dtype=np.float32)
     B, H, N, _ = x.shape
     nb64 = -(-N // 64)
     if block_rows == 0:
         amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
-        s = np.float32(amax) / np.float32(E4M3_MAX)
-        if amax == 0:
-            s = np.float32(1.0)
+        s = pow2_scale(np.float32(amax) / np.float32(E4M3_MAX))
         return np.full((B, H, nb64), s, dtype=np.float32)
     nb = -(-N // block_rows)
     out = np.empty((B, H, nb), dtype=np.float32)
     for i in range(nb):
         blk = np.abs(x[:, :, i * block_rows:(i + 1) * block_rows, :])
         amax = blk.max(axis=(2, 3)).astype(np.float32)
-        s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-        out[:, :, i] = np.where(amax == 0, np.float32(1.0), s)
+        out[:, :, i] = pow2_scale((amax / np.float32(E4M3_MAX)).astype(np.float32))
     return out
 
 

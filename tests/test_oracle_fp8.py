@@ -79,17 +79,41 @@ def test_block_scales_and_codes():
                 blk = xf[b, h, 64 * i:64 * (i + 1)]
                 amax = np.float32(np.abs(blk).max())
                 if amax > 0:
-                    assert s[b, h, i] == np.float32(amax / np.float32(448.0))
-                    # the largest element maps to the largest code
+                    r = np.float64(np.float32(amax / np.float32(448.0)))
+                    si = np.float64(s[b, h, i])
+                    # a power of two, the smallest at or above amax / 448
+                    assert np.frexp(si)[0] == 0.5
+                    assert r <= si < 2 * r
+                    # the largest element lands in (224, 448]: codes 0x76 .. 0x7E
                     cblk = codes[b, h, 64 * i:64 * (i + 1)]
-                    assert np.max(cblk & 0x7F) == 0x7E
+                    assert 0x76 <= np.max(cblk & 0x7F) <= 0x7E
     d = F.dequantize(codes, s, 64)
     srow = s[:, :, np.arange(150) // 64][..., None]
     assert np.all(np.abs(d - x) <= srow * 448 * 2.0 ** -4 + 1e-30)
     # per-tensor: one scale everywhere
     c0, s0, _ = F.quantize(x, 0)
     assert np.all(s0 == s0.flat[0])
-    assert s0.flat[0] == np.float32(np.float32(np.abs(x).max()) / np.float32(448))
+    r0 = np.float64(np.float32(np.float32(np.abs(x).max()) / np.float32(448)))
+    assert np.frexp(np.float64(s0.flat[0]))[0] == 0.5 and r0 <= s0.flat[0] < 2 * r0
+
+
+def test_pow2_scale():
+    """The block scale is the smallest power of two at or above its argument
+    (an exact power of two is kept), at least 2^-126, and 1 for zero."""
+    rng = np.random.default_rng(34)
+    r = np.concatenate([np.exp2(rng.uniform(-140, 120, 5000)), np.exp2(np.arange(-126, 120, 7.0)),
+                        np.nextafter(np.exp2(np.arange(-100, 100, 9.0)), 0), [0.0, 2.0 ** -149, 2.0 ** -127]])
+    r = r.astype(np.float32).astype(np.float64)
+    s = F.pow2_scale(r).astype(np.float64)
+    pos = r > 0
+    assert np.all(s[~pos] == 1.0)
+    assert np.all(np.frexp(s[pos])[0] == 0.5)                  # powers of two
+    assert np.all(s[pos] >= np.maximum(r[pos], 2.0 ** -126))
+    big = r > 2.0 ** -126
+    assert np.all(s[big] < 2 * r[big])                          # the smallest such
+    assert np.all(s[pos & ~big] == 2.0 ** -126)
+    exact = np.exp2(np.arange(-126, 120, 7.0))
+    assert np.all(F.pow2_scale(exact) == exact)
 
 
 def test_rotation_leaves_scores_unchanged_before_rounding():
