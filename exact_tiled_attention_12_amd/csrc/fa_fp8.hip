@@ -3,7 +3,9 @@
 //
 // What it computes ("FlashAttention v1～v4 完整进化史", v3 part 3):
 //   * each block of 64 rows (all d columns) of one (batch, head) gets its own
-//     scale s = amax / 448 instead of one scale for the whole tensor; Q and K
+//     scale instead of one scale for the whole tensor: the smallest power of
+//     two at or above amax / 448 (the form is not stated; a power of two
+//     divides exactly and is the fp8 matrix cores' block-scale form); Q and K
 //     may first be multiplied by one orthogonal matrix, which leaves Q K^T
 //     unchanged and spreads outlier channels over all columns;
 //   * both attention products run on fp8 matrix cores; the exponentiated
@@ -24,9 +26,10 @@
 //   * the scores are scaled by scale * log2(e) * sQ * sK_j in one FMA that
 //     also folds in the factor 448, so P' = 448 P~ comes out of exp2 ready to
 //     convert; l sums the float32 P' (the factor 448 cancels in O = acc / l);
-//   * the V block scale differs per tile, so the accumulator is kept in units
-//     of the current tile's scale: before tile j's product it is multiplied by
-//     alpha_j * sV_{j-1} / sV_j, and O = acc * sV_last / l at the end.
+//   * the V block scale of each tile goes into its product with P as the
+//     matrix instruction's 8-bit exponent scale of the V operand, so the
+//     accumulator stays in the units of O; it is multiplied by alpha only in
+//     steps where some row's maximum moved, and O = acc / l at the end.
 #include <cfloat>
 #include <type_traits>
 
@@ -85,9 +88,21 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
-// Four codes of y / s. With s a normal float32, s = amax / 448 rounded, so
-// |y / s| <= 448 (1 + 2^-23) and the hardware conversion is exact; a
-// subnormal s (a block of tiny values) takes the saturating encoder.
+// Block scale of a block whose largest magnitude is am: the smallest power
+// of two at or above float32(am / 448), at least 2^-126 (so a valid 8-bit
+// matrix-core exponent); 1 for an all-zero block.
+__device__ __forceinline__ float block_scale(float am) {
+  if (!(am > 0.f)) return 1.f;
+  uint32_t b = __float_as_uint(am / 448.f);   // correctly rounded float32 division
+  if (b < 0x00800000u) return FLT_MIN;         // at or below 2^-126
+  if (b & 0x007FFFFFu) b = (b & 0x7F800000u) + 0x00800000u;
+  return __uint_as_float(b);
+}
+
+// Four codes of y / s. s is a power of two at or above fl(amax / 448), so
+// y / s is exact (or a correctly rounded subnormal), |y / s| <= 448 (1 +
+// 2^-23) and the hardware conversion is exact; the saturating encoder is
+// kept for a subnormal s, which block_scale never gives.
 __device__ __forceinline__ uint32_t codes4(const float* y, float s, bool fast) {
   if (fast) return e4m3x4(y[0] / s, y[1] / s, y[2] / s, y[3] / s);
   return e4m3_code(y[0] / s) | e4m3_code(y[1] / s) << 8 | e4m3_code(y[2] / s) << 16 | e4m3_code(y[3] / s) << 24;
@@ -212,7 +227,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantArgs a, int nb
         if (tid == 0) *sc = am;
         continue;
       }
-      s = am == 0.f ? 1.f : am / 448.f;   // correctly rounded float32 division
+      s = block_scale(am);
       if (tid == 0) *sc = s;
     }
     if constexpr (ROT) {
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(kRedThreads) void quant_tensor_scale_kernel(float* 
   am = red[0];
 #pragma unroll
   for (int i = 1; i < kRedThreads / 64; ++i) am = fmaxf(am, red[i]);
-  const float s = am == 0.f ? 1.f : am / 448.f;
+  const float s = block_scale(am);
   for (int i = tid; i < n; i += kRedThreads) scales[i] = s;
 }
 
@@ -321,6 +336,13 @@ __device__ __forceinline__ f32x16 mma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same product with the A operand's blocks scaled by 2^(ea - 127) (an
+// 8-bit exponent, the biased exponent field of a power-of-two float) and
+// the B operand's by 2^0.
+__device__ __forceinline__ f32x16 mma_fp8_scale_a(i32x8 a, i32x8 b, f32x16 c, int ea) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, 127);
+}
+
 
 // Accumulator slot r of lane half h in 32-key block t holds key 32t + 16h + r
 // of the tile (the K rows are permuted to make it so). A position p of the A
@@ -360,9 +382,10 @@ __device__ __forceinline__ void ring_barrier() {
 // run S of tile j+1 and the product of tile j-1 with V; none of the step's 8
 // products depends on its vector work, so they are interleaved one product
 // at a time. The running maximum stays exact per tile (a stale maximum would
-// push 448 P past the e4m3 range). The accumulator is kept in units of the
-// current tile's V scale, so before the product of tile j-1 it is multiplied
-// by alpha_{j-1} sV_{j-2} / sV_{j-1}.
+// push 448 P past the e4m3 range). The V block scale of tile j-1 (a power
+// of two) scales the product of tile j-1 inside the matrix instruction, so
+// the accumulator is multiplied before that product only by alpha_{j-1}, and
+// only in steps where some row of the wave has alpha != 1.
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -441,8 +464,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   float m = -INFINITY;     // running maximum of this lane's row (scaled log2 units)
   float l = 0.f;           // sum of P' = 448 P~ over this lane half's keys
-  float sv_cur = 1.f;      // V scale of the newest tile the accumulator was brought to
-  float gam = 1.f;         // factor that brings the accumulator to the next tile's units
+  float gam = 1.f;         // alpha of the newest softmax tile: the accumulator's factor
+  bool resc = false;       // gam != 1 on some lane of the wave
+  int ev = 127;            // 8-bit exponent of the V scale of the newest softmax tile
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
@@ -500,10 +524,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   // One pipeline step: softmax of tile j (raw scores sc, fp8 P to pc), S of
   // tile j+1 into sn, and O += V^T P^T of tile j-1 (pp, V operands from the
-  // step's fetches). Accumulator block mt is brought to the units of tile
-  // j-1 (factor gam from the previous step) at position mt, before its
-  // product at position 4 + mt. mxr holds the raw row maximum of sc on entry
-  // (of the unmasked scores) and that of sn on exit.
+  // step's fetches, V scaled by its block scale in the instruction).
+  // Accumulator block mt is multiplied by alpha of tile j-1 (gam from the
+  // previous step) at position mt, before its product at position 4 + mt,
+  // when that alpha is not 1 on some lane. mxr holds the raw row maximum of
+  // sc on entry (of the unmasked scores) and that of sn on exit.
   auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], const i32x8& pp, i32x8& pc, Ops& cur, Ops& nxt,
                   const unsigned char* kt, const unsigned char* vt, const unsigned char* nkt,
                   const unsigned char* nvt, float skj, float svj_in, float& mxr) INL {
@@ -517,15 +542,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     // c_j > 0 keeps masked scores at -inf after scaling (scale 0 or an
     // underflowing product would turn -inf * 0 into NaN).
     const float cj = fmaxf(cq * skj, FLT_MIN);
-    const float svj = j < kv_end ? svj_in : sv_cur;
     const float m_new = fmaxf(m, mxr * cj);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
     const float gam_prev = gam;
+    const bool resc_prev = resc;
+    const int ev_prev = ev;
     m = m_new;
     l *= alpha;
     // P' = 2^(c_j s - m + log2 448) = 448 P~, four per position.
     const float nmo = kLog2_448 - m_use;
+    // alpha of tile j-1 on the accumulator, before its product with V
+    // below; skipped (most steps) when no row's maximum moved.
+    if (resc_prev) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) oacc[mt] *= gam_prev;
+    }
     f32x16 acc[2] = {f32x16{}, f32x16{}};
     float part[4];
     float hm0 = 0.f, hm1 = 0.f;
@@ -538,10 +570,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       if (p < 4) {
         const int tb = p / 2, ks = p % 2;
         acc[tb] = mma_fp8(cur.kf[p], qf[ks], acc[tb]);
-        oacc[p] *= gam_prev;
       } else {
         const int mt = p - 4;
-        oacc[mt] = mma_fp8(cur.vf[mt], pp, oacc[mt]);
+        oacc[mt] = mma_fp8_scale_a(cur.vf[mt], pp, oacc[mt], ev_prev);
       }
       // Scores 4p .. 4p+3: word p of the fp8 P operand.
       float e[4];
@@ -557,9 +588,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       // Uniform bookkeeping, and the next tile's row maximum once its S
       // products (positions 0..3) have completed.
       if (p == 0) {
-        gam = alpha * (sv_cur * __builtin_amdgcn_rcpf(svj));
-        pin(gam);
-        sv_cur = svj;
+        gam = alpha;
+        resc = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
+        // (a drain step past the last tile has no V: its P is all zero)
+        ev = j < kv_end ? (int)((__float_as_uint(svj_in) >> 23) & 0xFFu) : 127;
       }
       if (p == 5) hm0 = half_max(acc[0]);
       if (p == 6) hm1 = half_max(acc[1]);
@@ -671,7 +703,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   // O = acc * sV / l' and LSE = (m + log2 l' - log2 448) ln 2.
   const float lt = halves_sum(l);
-  const float inv = lt == 0.f ? 0.f : sv_cur / lt;
+  const float inv = lt == 0.f ? 0.f : 1.f / lt;
   if (qrow < N) {
     __bf16* og = (__bf16*)a.o + base + (size_t)qrow * kD;
 #pragma unroll

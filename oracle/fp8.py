@@ -124,14 +124,18 @@ def block_scales(x, block_rows: int) -> np.ndarray:
     nb64 = -(-N // 64)
     if block_rows == 0:
         amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
-        s = pow2_scale(np.float32(amax) / np.float32(E4M3_MAX))
+        r = np.float32(amax) / np.float32(E4M3_MAX)
+        s = pow2_scale(max(r, np.float32(2.0 ** -149)) if amax > 0 else np.float32(0))
         return np.full((B, H, nb64), s, dtype=np.float32)
     nb = -(-N // block_rows)
     out = np.empty((B, H, nb), dtype=np.float32)
     for i in range(nb):
         blk = np.abs(x[:, :, i * block_rows:(i + 1) * block_rows, :])
         amax = blk.max(axis=(2, 3)).astype(np.float32)
-        out[:, :, i] = pow2_scale((amax / np.float32(E4M3_MAX)).astype(np.float32))
+        r = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        # a nonzero block whose amax / 448 underflows to 0 still gets 2^-126
+        r = np.where(amax > 0, np.maximum(r, np.float32(2.0 ** -149)), np.float32(0))
+        out[:, :, i] = pow2_scale(r)
     return out
 
 

@@ -4,7 +4,8 @@
   oracle's codec (the division x / s is float32 on both sides).
 * Quantisation with rotation: the GPU forms x * rot in float32; its codes must
   lie within the codes of the exact product widened by the float32 summation
-  bound, and its scales within that bound of amax / 448.
+  bound, and its scales the powers of two at or above amax / 448 within that
+  bound.
 * fp8 attention: against the oracle's fp8 emulation on the same codes, element
   by element, within the bound of tests/fp8_bounds.py (the matrix cores' fp8
   accumulation, a few float32 roundings, e4m3 code flips they can cause, and
@@ -109,7 +110,10 @@ def test_quant_nan_element(fa, rotate):
         assert not np.any((rest & 0x7F) == 0x7F), "NaN codes outside the NaN row"
         y = clean.astype(np.float64) @ rot.astype(np.float64)
         amax = np.abs(np.delete(y[0, 1, 64:128], 70 - 64, axis=0)).max()
-        assert abs(got_s[0, 1, 1] - amax / 448) <= 1e-5 * amax / 448
+        # the block scale: the power of two at or above amax / 448 (amax of
+        # the float32 product, within 1e-5 of the exact one here)
+        near = {float(F.pow2_scale(np.float32(amax / 448 * f))) for f in (1 - 1e-5, 1 + 1e-5)}
+        assert float(got_s[0, 1, 1]) in near, (got_s[0, 1, 1], amax / 448)
     else:
         assert (got_c[0, 1, 70, 5] & 0x7F) == 0x7F, "NaN element not NaN-coded"
         codes_ref, s_ref, _ = F.quantize(clean, 64)
@@ -150,7 +154,11 @@ def test_quant_rotated(fa, d, N):
                 e = err[b, h, blk].max()
                 lo = (amax - e) / 448 * (1 - u)
                 hi = (amax + e) / 448 * (1 + u)
-                assert lo <= got_s[b, h, i] <= hi, (b, h, i, got_s[b, h, i], amax / 448)
+                # float32 amax / 448 lies in [lo, hi]; its scale is the power
+                # of two at or above it
+                s_lo, s_hi = (float(F.pow2_scale(np.float32(x))) for x in (lo, hi))
+                assert s_lo <= got_s[b, h, i] <= s_hi and np.frexp(got_s[b, h, i])[0] == 0.5, \
+                    (b, h, i, got_s[b, h, i], amax / 448)
     srow = np.repeat(got_s, 64, axis=2)[:, :, :N, None]
     qlo = (y - err) / srow * (1 - 2 * u)
     qhi = (y + err) / srow * (1 + 2 * u)
