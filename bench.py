@@ -62,6 +62,34 @@ def load_traffic(kernel_key, files, per_launch_units):
     return ent.get("hbm_bytes_per_launch")
 
 
+def load_counters(kernel_key, files):
+    """Clock and MFMA-busy figures from committed rocprofv3 counter summaries, if current.
+
+    The clock is GRBM_GUI_ACTIVE over the eight XCDs divided by the launch's
+    duration in the counter run; the fraction at that clock prices the
+    achieved rate against 1024 FLOP per SIMD per cycle (bf16) at that clock.
+    """
+    path = os.path.join(PROFILES, "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("src_sha") != kernel_source_sha(files):
+        return None
+    return ent
+
+
+def at_clock(achieved, peak, kernel_key, files):
+    """measured_clock_ghz, mfma_busy and frac_at_measured_clock for a roofline entry (None if stale)."""
+    c = load_counters(kernel_key, files)
+    if not c or "clock_ghz" not in c or "peak_tflops_at_measured_clock" not in c:
+        return {"measured_clock_ghz": None, "mfma_busy": None, "frac_at_measured_clock": None}
+    p = peak * c["clock_ghz"] / 2.4
+    return {"measured_clock_ghz": c["clock_ghz"], "mfma_busy": c.get("mfma_busy"),
+            "frac_at_measured_clock": round(achieved / p, 4)}
+
+
 def host_info():
     """Host cores and the BLAS library numpy runs the oracle's products on."""
     info = {"host_cpus": os.cpu_count()}
@@ -192,6 +220,9 @@ def configs_section(fa, which=(1, 2, 3)):
         res[f"workload_{k}"] = {"shape": [w.B, w.H, w.N, w.d], "dtype": w.dtype, "causal": w.causal,
                                 "fwd_ms": round(ms, 4), "fwd_tflops": round(tf, 2),
                                 "frac_of_peak": round(tf / peak, 4), "peak_tflops": peak}
+        ck = {2: "attn_fwd_bf16_d64_N1024_B8_H12", 3: "attn_fwd_bf16_d128_causal_N4096_B2_H32"}.get(k)
+        if ck:
+            res[f"workload_{k}"].update(at_clock(tf, peak, ck, ["fa_fwd_bf16.hip", "fa_device.h"]))
         del t, o, lse
     return res
 
@@ -250,7 +281,8 @@ def fp8_section(fa, steps: int, warmup: int):
             "quant_ms": round(q_ms, 4), "quant_gbps": round(q_gbs, 1),
             "quant_frac_of_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4),
             "fwd_ms": round(f_ms, 4), "fwd_tflops": round(tf, 2),
-            "fwd_frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+            "fwd_frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "fwd_at_clock": at_clock(tf, PEAK_FP8_TFLOPS, "attn_fwd_fp8_d128_N8192_B4_H32", ["fa_fp8.hip", "fa_device.h"])}
 
 
 def det_section(fa, q, k, v, o, lse, do, causal: bool, steps: int, warmup: int, bwd_ms: float):
@@ -494,6 +526,7 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic(f"{dom}_bf16_d128_causal_N16384_B1_H32", files, 1)}
+    roofline.update(at_clock(achieved, PEAK_BF16_TFLOPS, f"{dom}_bf16_d128_causal_N16384_B1_H32", files))
 
     out = {
         "metric": "attention fwd/bwd TFLOP/s at d=128 causal bf16, % of MFMA peak (1 GPU)",
@@ -516,7 +549,10 @@ def main():
                       "bwd_pre_ms": round(bwd_pre_ms, 4), "bwd_main_ms": round(bwd_main_ms, 4),
                       "bwd_finish_ms": round(bwd_fin_ms, 4),
                       "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
-                      "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if do_bwd else None},
+                      "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if do_bwd else None,
+                      "fwd_at_clock": at_clock(f_fwd / (fwd_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS,
+                                               "attn_fwd_bf16_d128_causal_N16384_B1_H32",
+                                               ["fa_fwd_bf16.hip", "fa_device.h"])},
         "roofline": roofline,
     }
     if do_bwd and not args.no_det:
