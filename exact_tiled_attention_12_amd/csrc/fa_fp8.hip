@@ -325,9 +325,10 @@ constexpr float kLog2_448 = 8.807354922057604f;
 __device__ __forceinline__ int k_swz(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
 __device__ __forceinline__ int v_swz(int r) { return r & 6; }
 
-__device__ __forceinline__ u32x2 tr8_read(const unsigned char* lds_byte_ptr) {
+// Transposed 8-byte read at LDS byte address addr.
+__device__ __forceinline__ u32x2 tr8_read(unsigned addr) {
   typedef int i32x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, lds_byte_ptr)));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, addr)));
 }
 
 __device__ __forceinline__ f32x16 mma_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -354,6 +355,13 @@ __device__ __forceinline__ int pos_to_key(int p) { return 16 * ((p >> 2) & 1) + 
 // extra instruction per score.
 __device__ __forceinline__ float max3(float a, float b, float c) {
   return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+}
+
+// The larger of the two lane halves' values (lanes l and l ^ 32), as one
+// v_maximum3_f32 after the swap: fmaxf would first quiet both swapped words.
+__device__ __forceinline__ float halves_maximum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max3(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
 }
 
 // Materialises x at this point of the instruction stream: values produced in
@@ -479,24 +487,49 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     i32x8 kf[4];
     i32x8 vf[4];
   };
-  auto fetch = [&](int p, Ops& o, const unsigned char* kt, const unsigned char* vt) INL {
+  // LDS byte addresses of this lane's fragments in stage 0 and in stage 4:
+  // the rest of a read's address (stage within its half of the ring, key
+  // block, transposed-read group) fits the 16-bit immediate offset of the
+  // LDS read, but the lane's swizzled part does not combine with it by an
+  // addition, so each variant is formed once here and held in registers
+  // (pinned: otherwise the compiler re-forms them in every step, one VALU
+  // instruction and one hazard wait per read). K: [stage half][d step ks]
+  // [16-byte half]; V: [stage half][d block mt].
+  const unsigned ring0 = (unsigned)(uintptr_t)LDS(unsigned char, ring);
+  unsigned kadr[2][2][2], vadr[2][4];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        kadr[hi][ks][hb] = ring0 + hi * 4 * kStage + ((k_lane ^ (64u * ks)) ^ (16u * hb));
+        pin(kadr[hi][ks][hb]);
+      }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      vadr[hi][mt] = ring0 + hi * 4 * kStage + kTile + (v_lane ^ (32u * mt));
+      pin(vadr[hi][mt]);
+    }
+  }
+  // Operands of position p from K of stage kst and V of stage vst.
+  auto fetch = [&](int p, Ops& o, int kst, int vst) INL {
     if (p < 4) {
       const int tb = p / 2, ks = p % 2;
-      const unsigned a0 = (k_lane ^ (64u * ks)) + tb * 32 * kRB;
-      const u32x4 lo = *LDS(u32x4, kt + a0);
-      const u32x4 hi = *LDS(u32x4, kt + (a0 ^ 16u));
+      const unsigned off = (unsigned)((kst & 3) * kStage + tb * 32 * kRB);
+      const u32x4 lo = *LDS(u32x4, kadr[kst >> 2][ks][0] + off);
+      const u32x4 hi = *LDS(u32x4, kadr[kst >> 2][ks][1] + off);
       o.kf[p] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     } else {
       const int mt = p - 4;
       u32x2 vr[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) vr[q] = tr8_read(vt + (v_lane ^ (32u * mt)) + 4096 * (q >> 1) + 1024 * (q & 1));
+      for (int q = 0; q < 4; ++q)
+        vr[q] = tr8_read(vadr[vst >> 2][mt] + (unsigned)((vst & 3) * kStage + 4096 * (q >> 1) + 1024 * (q & 1)));
       o.vf[mt] = i32x8{(int)vr[0][0], (int)vr[0][1], (int)vr[1][0], (int)vr[1][1],
                        (int)vr[2][0], (int)vr[2][1], (int)vr[3][0], (int)vr[3][1]};
     }
   };
-  auto ktile = [&](auto kst) INL -> const unsigned char* { return sp(kst); };
-  auto vtile = [&](auto vst) INL -> const unsigned char* { return sp(vst) + kTile; };
   constexpr int AHEAD = 3;
 
   // Scores of tile j past N or (causal) above the diagonal -> -inf; needed on
@@ -519,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     return max3(a0, max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]));
   };
   auto row_max = [&](const f32x16 (&x)[2]) INL -> float {
-    return halves_max(max3(half_max(x[0]), half_max(x[1]), fmaxf(x[0][15], x[1][15])));
+    return halves_maximum(max3(half_max(x[0]), half_max(x[1]), max3(x[0][15], x[1][15], x[1][15])));
   };
 
   // One pipeline step: softmax of tile j (raw scores sc, fp8 P to pc), S of
@@ -530,8 +563,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   // when that alpha is not 1 on some lane. mxr holds the raw row maximum of
   // sc on entry (of the unmasked scores) and that of sn on exit.
   auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], const i32x8& pp, i32x8& pc, Ops& cur, Ops& nxt,
-                  const unsigned char* kt, const unsigned char* vt, const unsigned char* nkt,
-                  const unsigned char* nvt, float skj, float svj_in, float& mxr) INL {
+                  int kst, int vst, int nkst, int nvst, float skj, float svj_in, float& mxr) INL {
     if (masked(j)) {
       apply_mask(j, sc);
       mxr = row_max(sc);
@@ -542,7 +574,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     // c_j > 0 keeps masked scores at -inf after scaling (scale 0 or an
     // underflowing product would turn -inf * 0 into NaN).
     const float cj = fmaxf(cq * skj, FLT_MIN);
-    const float m_new = fmaxf(m, mxr * cj);
+    const float m_new = max3(m, mxr * cj, mxr * cj);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
     const float gam_prev = gam;
@@ -564,9 +596,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       if (p + AHEAD < 8)
-        fetch(p + AHEAD, cur, kt, vt);
+        fetch(p + AHEAD, cur, kst, vst);
       else
-        fetch(p + AHEAD - 8, nxt, nkt, nvt);
+        fetch(p + AHEAD - 8, nxt, nkst, nvst);
       if (p < 4) {
         const int tb = p / 2, ks = p % 2;
         acc[tb] = mma_fp8(cur.kf[p], qf[ks], acc[tb]);
@@ -581,7 +613,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
         e[i] = fast_exp2(__builtin_fmaf(sc[p >> 2][4 * (p & 3) + i], cj, nmo));
         part[i] = p == 0 ? e[i] : part[i] + e[i];
       }
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      // The low half is converted into an undefined word (the high half is
+      // written next), which spares a register clear per word.
+      int word;
+      asm volatile("" : "=v"(word));
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], word, false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], word, true);
       pin(word);
       pc[p] = word;
@@ -595,7 +631,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       }
       if (p == 5) hm0 = half_max(acc[0]);
       if (p == 6) hm1 = half_max(acc[1]);
-      if (p == 7) mxr = halves_max(max3(hm0, hm1, fmaxf(acc[0][15], acc[1][15])));
+      if (p == 7) mxr = halves_maximum(max3(hm0, hm1, max3(acc[0][15], acc[1][15], acc[1][15])));
       __builtin_amdgcn_sched_barrier(0);
     }
     sn[0] = acc[0];
@@ -631,7 +667,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   i32x8 pa, pb = i32x8{};
   Ops oa, ob;
   {
-    const unsigned char* kt = ktile(IC<0>{});
+    const unsigned char* kt = sp(IC<0>{});
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       f32x16 acc = f32x16{};
@@ -648,8 +684,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   }
   float mxr = row_max(sa);
 #pragma unroll
-  for (int p = 0; p < AHEAD; ++p) fetch(p, oa, ktile(IC<1>{}), vtile(IC<0>{}));
-  step(0, sa, sb, pb, pa, oa, ob, ktile(IC<1>{}), vtile(IC<0>{}), ktile(IC<2>{}), vtile(IC<0>{}), sk[0], sv[0], mxr);
+  for (int p = 0; p < AHEAD; ++p) fetch(p, oa, 1, 0);
+  step(0, sa, sb, pb, pa, oa, ob, 1, 0, 2, 0, sk[0], sv[0], mxr);
 
   // Scales of tiles j0 .. j0+7 (indices clamped to the last block: past
   // kv_end they are not used).
@@ -673,14 +709,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     constexpr int S = decltype(s_tag)::value;   // j = j0 + S, j0 = 1 (mod 8)
     const int j = j0 + S;
     if constexpr (S % 2 == 1) pair_sync(j, IC<(S + 6) % kStages>{}, IC<(S + 7) % kStages>{});
-    const unsigned char* kt = ktile(IC<(S + 2) % kStages>{});
-    const unsigned char* vt = vtile(IC<S % kStages>{});
-    const unsigned char* nkt = ktile(IC<(S + 3) % kStages>{});
-    const unsigned char* nvt = vtile(IC<(S + 1) % kStages>{});
+    constexpr int kst = (S + 2) % kStages, vst = S % kStages;
+    constexpr int nkst = (S + 3) % kStages, nvst = (S + 1) % kStages;
     if constexpr (S % 2 == 0)
-      step(j, sb, sa, pa, pb, ob, oa, kt, vt, nkt, nvt, skc[S], svc[S], mxr);
+      step(j, sb, sa, pa, pb, ob, oa, kst, vst, nkst, nvst, skc[S], svc[S], mxr);
     else
-      step(j, sa, sb, pb, pa, oa, ob, kt, vt, nkt, nvt, skc[S], svc[S], mxr);
+      step(j, sa, sb, pb, pa, oa, ob, kst, vst, nkst, nvst, skc[S], svc[S], mxr);
     return j == kv_end;
   };
   for (int j0 = 1;; j0 += kStages) {
