@@ -18,17 +18,23 @@ Sources:
   * Block granularity is not stated. Reading: one scale per 64 consecutive
     rows (all d columns) of one (batch, head). Per-tensor baseline: one s
     for the whole tensor.
-  * The form of a block's scale is not stated either. Reading: s is the
-    smallest power of two at or above amax / 448 (amax / 448 first rounded
-    to float32), kept at or above 2^-126; s = 1 when the block is all zero.
-    A power of two divides exactly (the only rounding is the e4m3 one), the
-    block's largest element lands in (224, 448], and it is the form the fp8
-    matrix cores accept as a block scale (an 8-bit exponent), so the product
-    with V can be scaled block by block without touching the accumulator.
+  * The form of a block's scale is not stated either. Reading: s = amax /
+    448 (float32(amax) / 448 rounded to float32), which puts the block's
+    largest magnitude on the largest code; s = 1 when the block is all zero,
+    and a nonzero block whose amax / 448 underflows gets 2^-149 (the
+    smallest positive float32). A second form (pow2=True) takes the
+    smallest power of two at or above that value, kept at or above 2^-126:
+    it is the form the fp8 matrix cores accept as a block scale (an 8-bit
+    exponent), so the product with V can be scaled tile by tile inside the
+    instruction without touching the accumulator. The GPU path quantises V
+    in that form and Q, K in the plain one. Measured with this oracle
+    (oracle/fp8_granularity.py, the 4 x 32 x 8192 x 128 workload, 8 heads,
+    rotated Q and K): RMSE of O 0.2311 with every scale plain, 0.2309 with
+    V's a power of two, 0.2534 with all three powers of two (a power of two
+    costs Q and K the exact top code of every block).
   * Where a float decides a code (the division x / s), it is taken in
-    float32, the precision the GPU quantiser uses; s is derived from
-    float32(amax) / 448 rounded to float32 (and x / s is exact, s being a
-    power of two).
+    float32, the precision the GPU quantiser uses (x / s is exact when s is
+    a power of two).
 
 Pins: tests/test_oracle_fp8.py (all 65,536 bf16 bit patterns against the
 CPU library cast to float8_e4m3fn, hand-decoded codes, scale properties).
@@ -110,11 +116,24 @@ def pow2_scale(r) -> np.ndarray:
     return np.where(r > 0, s, 1.0).astype(np.float32)
 
 
-def block_scales(x, block_rows: int) -> np.ndarray:
+def _scale_of(amax, pow2: bool) -> np.ndarray:
+    """Scale of blocks with largest magnitudes amax (float32 array)."""
+    amax = np.asarray(amax, dtype=np.float32)
+    r = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    # a nonzero block whose amax / 448 underflows to 0 gets the smallest
+    # positive float32 (2^-126 in the power-of-two form)
+    r = np.where(amax > 0, np.maximum(r, np.float32(2.0 ** -149)), np.float32(0)).astype(np.float32)
+    if pow2:
+        return pow2_scale(r)
+    return np.where(amax > 0, r, np.float32(1.0)).astype(np.float32)
+
+
+def block_scales(x, block_rows: int, pow2: bool = False) -> np.ndarray:
     """Block scales in float32 for x of shape [B, H, N, d].
 
-    s = the smallest power of two at or above float32(amax) / 448 (rounded to
-    float32), at least 2^-126; s = 1 for an all-zero block.
+    s = float32(amax) / 448 rounded to float32 (1 for an all-zero block,
+    2^-149 where that quotient underflows); with pow2, the smallest power of
+    two at or above it, at least 2^-126 (1 for an all-zero block).
     block_rows > 0: one scale per block of ``block_rows`` rows of each
     (batch, head), shape [B, H, ceil(N / block_rows)]. block_rows == 0: one
     scale for the whole tensor, returned broadcast to shape [B, H, ceil(N/64)].
@@ -124,18 +143,12 @@ def block_scales(x, block_rows: int) -> np.ndarray:
     nb64 = -(-N // 64)
     if block_rows == 0:
         amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
-        r = np.float32(amax) / np.float32(E4M3_MAX)
-        s = pow2_scale(max(r, np.float32(2.0 ** -149)) if amax > 0 else np.float32(0))
-        return np.full((B, H, nb64), s, dtype=np.float32)
+        return np.full((B, H, nb64), _scale_of(amax, pow2), dtype=np.float32)
     nb = -(-N // block_rows)
     out = np.empty((B, H, nb), dtype=np.float32)
     for i in range(nb):
         blk = np.abs(x[:, :, i * block_rows:(i + 1) * block_rows, :])
-        amax = blk.max(axis=(2, 3)).astype(np.float32)
-        r = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-        # a nonzero block whose amax / 448 underflows to 0 still gets 2^-126
-        r = np.where(amax > 0, np.maximum(r, np.float32(2.0 ** -149)), np.float32(0))
-        out[:, :, i] = pow2_scale(r)
+        out[:, :, i] = _scale_of(blk.max(axis=(2, 3)).astype(np.float32), pow2)
     return out
 
 
@@ -144,20 +157,22 @@ def _expand_rows(s, N, block_rows):
     return s[:, :, idx]
 
 
-def quantize(x, block_rows: int, rot=None):
-    """Quantise x [B, H, N, d] to e4m3 codes with per-block scales.
+def quantize(x, block_rows: int, rot=None, pow2: bool = False):
+    """Quantise x [B, H, N, d] to e4m3 codes with per-block scales
+    (``block_scales``; pow2 selects the power-of-two form).
 
     With ``rot`` (d x d), x is first multiplied by it on the right, in
     float64, and the product rounded to float32 (the GPU forms it in float32
     in a different summation order; codes are compared with that in mind).
-    The division x / s is taken in float32. Returns (codes uint8, scales f32,
+    The division x / s is taken in float32 (a quotient past 448 saturates).
+    Returns (codes uint8, scales f32,
     the float32 values that were quantised).
     """
     x = np.asarray(x, dtype=np.float64)
     if rot is not None:
         x = x @ np.asarray(rot, dtype=np.float64)
     xf = x.astype(np.float32)
-    s = block_scales(xf, block_rows)
+    s = block_scales(xf, block_rows, pow2)
     br = block_rows if block_rows > 0 else 64
     srow = _expand_rows(s, xf.shape[2], br)[..., None].astype(np.float32)
     y = (xf / srow).astype(np.float32)

@@ -66,11 +66,12 @@ def test_roundtrip_error_is_half_step():
     assert np.all(np.abs(y - x) <= half_step * (1 + 1e-12))
 
 
-def test_block_scales_and_codes():
+@pytest.mark.parametrize("pow2", [False, True])
+def test_block_scales_and_codes(pow2):
     rng = np.random.default_rng(32)
     x = rng.standard_normal((2, 3, 150, 16)).astype(np.float32)
     x[1, 2, 64:128] = 0.0
-    codes, s, xf = F.quantize(x, 64)
+    codes, s, xf = F.quantize(x, 64, pow2=pow2)
     assert s.shape == (2, 3, 3)
     assert s[1, 2, 1] == 1.0
     for b in range(2):
@@ -81,20 +82,44 @@ def test_block_scales_and_codes():
                 if amax > 0:
                     r = np.float64(np.float32(amax / np.float32(448.0)))
                     si = np.float64(s[b, h, i])
-                    # a power of two, the smallest at or above amax / 448
-                    assert np.frexp(si)[0] == 0.5
-                    assert r <= si < 2 * r
-                    # the largest element lands in (224, 448]: codes 0x76 .. 0x7E
                     cblk = codes[b, h, 64 * i:64 * (i + 1)]
-                    assert 0x76 <= np.max(cblk & 0x7F) <= 0x7E
+                    if pow2:
+                        # a power of two, the smallest at or above amax / 448
+                        assert np.frexp(si)[0] == 0.5
+                        assert r <= si < 2 * r
+                        # the largest element lands in (224, 448]: codes 0x76 .. 0x7E
+                        assert 0x76 <= np.max(cblk & 0x7F) <= 0x7E
+                    else:
+                        # amax / 448 itself: the largest element gets the top code
+                        assert si == r
+                        assert np.max(cblk & 0x7F) == 0x7E
     d = F.dequantize(codes, s, 64)
     srow = s[:, :, np.arange(150) // 64][..., None]
     assert np.all(np.abs(d - x) <= srow * 448 * 2.0 ** -4 + 1e-30)
     # per-tensor: one scale everywhere
-    c0, s0, _ = F.quantize(x, 0)
+    c0, s0, _ = F.quantize(x, 0, pow2=pow2)
     assert np.all(s0 == s0.flat[0])
     r0 = np.float64(np.float32(np.float32(np.abs(x).max()) / np.float32(448)))
-    assert np.frexp(np.float64(s0.flat[0]))[0] == 0.5 and r0 <= s0.flat[0] < 2 * r0
+    if pow2:
+        assert np.frexp(np.float64(s0.flat[0]))[0] == 0.5 and r0 <= s0.flat[0] < 2 * r0
+    else:
+        assert s0.flat[0] == r0
+
+
+def test_block_scale_edge_cases():
+    """All-zero blocks get 1; a block whose amax / 448 underflows gets the
+    smallest positive float32 (2^-126 in the power-of-two form), so nonzero
+    elements still get nonzero codes and zeros stay zero."""
+    x = np.zeros((1, 1, 128, 4), np.float32)
+    x[0, 0, 64, 0] = np.float32(2.0 ** -148)       # amax / 448 underflows
+    x[0, 0, 65, 1] = -np.float32(2.0 ** -149)
+    c, s, _ = F.quantize(x, 64)
+    assert s[0, 0, 0] == 1.0 and s[0, 0, 1] == np.float32(2.0 ** -149)
+    assert np.all(c[0, 0, :64] == 0)
+    assert c[0, 0, 64, 0] != 0 and c[0, 0, 65, 1] & 0x7F != 0 and c[0, 0, 65, 1] & 0x80
+    assert np.all(c[0, 0, 64, 1:] == 0)
+    c2, s2, _ = F.quantize(x, 64, pow2=True)
+    assert s2[0, 0, 0] == 1.0 and s2[0, 0, 1] == np.float32(2.0 ** -126)
 
 
 def test_pow2_scale():
