@@ -156,11 +156,11 @@ def oracle_configs():
         if k == 5:
             q8, sq, _ = F.quantize(x["q"], 64, x["rot"])
             k8, sk, _ = F.quantize(x["k"], 64, x["rot"])
-            v8, sv, _ = F.quantize(x["v"], 64)
+            v8, sv, _ = F.quantize(x["v"], 64, pow2=True)
             F.fp8_attention_tiled(q8, sq, k8, sk, v8, sv, w.scale, w.causal)
             q8, sq, _ = F.quantize(x["q"], 0)
             k8, sk, _ = F.quantize(x["k"], 0)
-            v8, sv, _ = F.quantize(x["v"], 0)
+            v8, sv, _ = F.quantize(x["v"], 0, pow2=True)
             F.fp8_attention_tiled(q8, sq, k8, sk, v8, sv, w.scale, w.causal)
             A.forward(x["q"], x["k"], x["v"], w.scale, w.causal)
         else:
@@ -257,7 +257,7 @@ def fp8_section(fa, steps: int, warmup: int):
             e[0].record()
         q8, sq = fa.quant_fp8(x["q"], rot=rot)
         k8, sk = fa.quant_fp8(x["k"], rot=rot)
-        v8, sv = fa.quant_fp8(x["v"])
+        v8, sv = fa.quant_fp8(x["v"], pow2=True)
         if e:
             e[1].record()
         fa.fwd_fp8(q8, k8, v8, sq, sk, sv, causal=False, scale=w.scale)

@@ -46,7 +46,7 @@ SIGNATURES = {
     "fa_bwd_noalloc_scratch_bytes": (_c_size, []),
     "fa_bwd_f32": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
-    "fa_quant_fp8": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),
+    "fa_quant_fp8": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),
     "fa_fwd_fp8": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _p, _p,
                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),

@@ -263,8 +263,11 @@ def bwd_stages(q, k, v, o, lse, do, workspace, dq, dk, dv, stage_mask: int, caus
     _lib.check(st, "fa_bwd_stages")
 
 
-def quant_fp8(x, rot=None, block_rows: int = 64, x8=None, scales=None):
-    """e4m3 codes (uint8) and per-64-row float32 scales of x (bf16 [B,H,N,d])."""
+def quant_fp8(x, rot=None, block_rows: int = 64, x8=None, scales=None, pow2: bool = False):
+    """e4m3 codes (uint8) and per-64-row float32 scales of x (bf16 [B,H,N,d]).
+
+    Scales are amax / 448, or with pow2 the smallest power of two at or above
+    it (the form fwd_fp8 requires for V)."""
     B, H, N, d = _shape4(x)
     _check_tensor(x, "x", torch.bfloat16, (B, H, N, d))
     if rot is not None:
@@ -275,7 +278,8 @@ def quant_fp8(x, rot=None, block_rows: int = 64, x8=None, scales=None):
     _check_tensor(x8, "x8", torch.uint8, (B, H, N, d))
     _check_tensor(scales, "scales", torch.float32, (B, H, nb))
     st = _lib.load().fa_quant_fp8(x.data_ptr(), rot.data_ptr() if rot is not None else None,
-                                  x8.data_ptr(), scales.data_ptr(), B, H, N, d, int(block_rows), _stream(x))
+                                  x8.data_ptr(), scales.data_ptr(), B, H, N, d, int(block_rows), int(bool(pow2)),
+                                  _stream(x))
     _lib.check(st, "fa_quant_fp8")
     return x8, scales
 
@@ -283,7 +287,9 @@ def quant_fp8(x, rot=None, block_rows: int = 64, x8=None, scales=None):
 def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = None, out=None, lse=None,
             block_rows: int = 64):
     """O (bf16), LSE from e4m3 codes with per-64-row scales (block_rows = 64)
-    or one per-tensor scale broadcast in the same layout (block_rows = 0)."""
+    or one per-tensor scale broadcast in the same layout (block_rows = 0).
+    sv must hold powers of two (quant_fp8(v, pow2=True)); a 256-row query
+    tile whose keys meet any other V scale comes out NaN."""
     B, H, N, d = _shape4(q8)
     nb = (N + 63) // 64
     for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):

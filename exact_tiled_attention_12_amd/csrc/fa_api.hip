@@ -393,18 +393,19 @@ int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, c
 }
 
 int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, float* scales, int B, int H, int N, int d,
-                 int block_rows, void* stream) {
+                 int block_rows, int pow2, void* stream) {
   int rc = check_shape(B, H, N, d, 1.f);
   if (rc) return rc;
   if (block_rows != 64 && block_rows != 0)
     return fail(FA_ERR_UNSUPPORTED, "block_rows must be 64 or 0 (got %d)", block_rows);
+  if (pow2 != 0 && pow2 != 1) return fail(FA_ERR_INVALID, "pow2 must be 0 or 1 (got %d)", pow2);
   const size_t n = (size_t)B * H * N * d;
   const size_t sb = (size_t)B * H * ((N + 63) / 64) * 4;
   const Buf in_r[2] = {{x, n * 2, "x", 16}, {rot, (size_t)d * d * 4, "rot", 16}};
   const Buf out[2] = {{x8, n, "x8", 16}, {scales, sb, "scales", 4}};
   rc = check_bufs(in_r, rot ? 2 : 1, out, 2);
   if (rc) return rc;
-  fa::QuantArgs a{x, rot, x8, scales, N, block_rows};
+  fa::QuantArgs a{x, rot, x8, scales, N, block_rows, pow2};
   return launched(fa::launch_quant_fp8(d, a, B, H, (hipStream_t)stream), "fp8 quantisation");
 }
 

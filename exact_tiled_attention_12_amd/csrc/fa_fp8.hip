@@ -3,11 +3,11 @@
 //
 // What it computes ("FlashAttention v1～v4 完整进化史", v3 part 3):
 //   * each block of 64 rows (all d columns) of one (batch, head) gets its own
-//     scale instead of one scale for the whole tensor: the smallest power of
-//     two at or above amax / 448 (the form is not stated; a power of two
-//     divides exactly and is the fp8 matrix cores' block-scale form); Q and K
-//     may first be multiplied by one orthogonal matrix, which leaves Q K^T
-//     unchanged and spreads outlier channels over all columns;
+//     scale instead of one scale for the whole tensor: amax / 448, or (the
+//     form is not stated; V takes this one) the smallest power of two at or
+//     above it, the fp8 matrix cores' block-scale form; Q and K may first be
+//     multiplied by one orthogonal matrix, which leaves Q K^T unchanged and
+//     spreads outlier channels over all columns;
 //   * both attention products run on fp8 matrix cores; the exponentiated
 //     scores are themselves rounded to fp8 for the product with V.
 // Format: OCP e4m3fn (bias 7, largest finite 448, no infinity); encoding
@@ -88,21 +88,23 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
-// Block scale of a block whose largest magnitude is am: the smallest power
-// of two at or above float32(am / 448), at least 2^-126 (so a valid 8-bit
-// matrix-core exponent); 1 for an all-zero block.
-__device__ __forceinline__ float block_scale(float am) {
+// Scale of a block whose largest magnitude is am: float32(am / 448) (a
+// correctly rounded division; the smallest positive float32 where it
+// underflows), or with pow2 the smallest power of two at or above it, at
+// least 2^-126 (a valid 8-bit matrix-core exponent); 1 for an all-zero block.
+__device__ __forceinline__ float block_scale(float am, bool pow2) {
   if (!(am > 0.f)) return 1.f;
-  uint32_t b = __float_as_uint(am / 448.f);   // correctly rounded float32 division
+  uint32_t b = __float_as_uint(am / 448.f);
+  if (!pow2) return b ? __uint_as_float(b) : __uint_as_float(1u);
   if (b < 0x00800000u) return FLT_MIN;         // at or below 2^-126
   if (b & 0x007FFFFFu) b = (b & 0x7F800000u) + 0x00800000u;
   return __uint_as_float(b);
 }
 
-// Four codes of y / s. s is a power of two at or above fl(amax / 448), so
-// y / s is exact (or a correctly rounded subnormal), |y / s| <= 448 (1 +
-// 2^-23) and the hardware conversion is exact; the saturating encoder is
-// kept for a subnormal s, which block_scale never gives.
+// Four codes of y / s. With s a normal float32 at or above fl(amax / 448),
+// |y / s| <= 448 (1 + 2^-23) and the hardware conversion is exact (with a
+// power of two, y / s itself is exact); a subnormal s (a block of tiny
+// values) takes the saturating encoder.
 __device__ __forceinline__ uint32_t codes4(const float* y, float s, bool fast) {
   if (fast) return e4m3x4(y[0] / s, y[1] / s, y[2] / s, y[3] / s);
   return e4m3_code(y[0] / s) | e4m3_code(y[1] / s) << 8 | e4m3_code(y[2] / s) << 16 | e4m3_code(y[3] / s) << 24;
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantArgs a, int nb
         if (tid == 0) *sc = am;
         continue;
       }
-      s = block_scale(am);
+      s = block_scale(am, a.pow2 != 0);
       if (tid == 0) *sc = s;
     }
     if constexpr (ROT) {
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantArgs a, int nb
 // Per-tensor scale: the largest of the per-block amax values written by the
 // kAmaxOnly pass, turned into s and broadcast to every block entry.
 constexpr int kRedThreads = 1024;
-__global__ __launch_bounds__(kRedThreads) void quant_tensor_scale_kernel(float* scales, int n) {
+__global__ __launch_bounds__(kRedThreads) void quant_tensor_scale_kernel(float* scales, int n, int pow2) {
   const int tid = threadIdx.x;
   float am = 0.f;
   for (int i = tid; i < n; i += kRedThreads) am = fmaxf(am, scales[i]);
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(kRedThreads) void quant_tensor_scale_kernel(float* 
   am = red[0];
 #pragma unroll
   for (int i = 1; i < kRedThreads / 64; ++i) am = fmaxf(am, red[i]);
-  const float s = block_scale(am);
+  const float s = block_scale(am, pow2 != 0);
   for (int i = tid; i < n; i += kRedThreads) scales[i] = s;
 }
 
@@ -296,7 +298,7 @@ hipError_t launch_quant_d(const QuantArgs& a, int B, int H, hipStream_t st) {
   hipLaunchKernelGGL((quant_kernel<D, ROT, kAmaxOnly>), dim3(grid), dim3(kQThreads), 0, st, a, nb, total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(quant_tensor_scale_kernel, dim3(1), dim3(kRedThreads), 0, st, a.scales, total);
+  hipLaunchKernelGGL(quant_tensor_scale_kernel, dim3(1), dim3(kRedThreads), 0, st, a.scales, total, a.pow2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((quant_kernel<D, ROT, kGivenScale>), dim3(grid), dim3(kQThreads), 0, st, a, nb, total);
@@ -735,9 +737,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
+  // Only the exponent of a V scale enters the instruction, so the V scales
+  // of the visited tiles must be powers of two in [2^-126, 2^127]; any other
+  // value turns this workgroup's rows into NaN instead of being rounded
+  // down. Checked here, off the loop, one tile per lane.
+  bool bad_v = false;
+  for (int j0 = 0; j0 < kv_end; j0 += 64) {
+    const int jj = j0 + lane;
+    const uint32_t vb = jj < kv_end ? __float_as_uint(a.sv[(size_t)bh * nb + jj]) : 0x3F800000u;
+    const uint32_t e8 = (vb >> 23) & 0xFFu;
+    const bool bad = (vb & 0x807FFFFFu) != 0u || e8 == 0u || e8 == 255u;
+    bad_v |= __builtin_amdgcn_ballot_w64(bad) != 0;
+  }
+
   // O = acc * sV / l' and LSE = (m + log2 l' - log2 448) ln 2.
   const float lt = halves_sum(l);
-  const float inv = lt == 0.f ? 0.f : 1.f / lt;
+  const float inv = bad_v ? __builtin_nanf("") : lt == 0.f ? 0.f : 1.f / lt;
   if (qrow < N) {
     __bf16* og = (__bf16*)a.o + base + (size_t)qrow * kD;
 #pragma unroll
@@ -750,7 +765,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
         *(u32x2*)(og + mt * 32 + 8 * g + 4 * hh) = w;
       }
     if (hh == 0)
-      a.lse[(size_t)bh * N + qrow] = lt == 0.f ? -INFINITY : (m + fast_log2(lt) - kLog2_448) * kLn2;
+      a.lse[(size_t)bh * N + qrow] = bad_v ? __builtin_nanf("")
+                                     : lt == 0.f ? -INFINITY : (m + fast_log2(lt) - kLog2_448) * kLn2;
   }
 #endif
 }

@@ -69,6 +69,7 @@ struct QuantArgs {
   float* scales;       // [B,H,ceil(N/64)]
   int N;
   int block_rows;      // 64 or 0
+  int pow2;            // 1: power-of-two scales; 0: amax / 448
 };
 
 struct Fp8FwdArgs {

@@ -249,18 +249,21 @@ FA_API int fa_bwd_f32(const float* q, const float* k, const float* v, const floa
  * block_rows = 64: one scale per 64 rows x d of each (b,h);
  * block_rows = 0: one scale for the whole tensor (the per-tensor baseline).
  * scales: [B,H,ceil(N/64)] float32 (written; with block_rows = 0 every entry
- * holds the same value). s is the smallest power of two at or above
- * amax / 448 (amax / 448 rounded to float32 first), at least 2^-126; 1 for
- * an all-zero block (the form of the scale is not stated on the page; a
- * power of two divides exactly and is the block-scale form of the fp8
- * matrix instructions); x8 = e4m3fn(x / s), rounded to nearest even after
- * saturating to +-448 (x8: [B,H,N,d] bytes, written). Inputs are expected finite: a NaN element gets a NaN code
- * (0x7F or 0xFF) and is left out of its block's amax (with rot, every
- * element of its row is NaN after the product and is treated so).
- * block_rows = 0 runs three launches and uses scales as scratch between
+ * holds the same value). The form of the scale is not stated on the page:
+ * pow2 = 0 gives s = amax / 448 (a correctly rounded float32 division; the
+ * smallest positive float32 where it underflows), which puts the block's
+ * largest magnitude on the top code; pow2 = 1 gives the smallest power of
+ * two at or above that value, at least 2^-126 (the block-scale form of the
+ * fp8 matrix instructions, which fa_fwd_fp8 requires for V); 1 for an
+ * all-zero block in both forms. Other pow2 values give FA_ERR_INVALID.
+ * x8 = e4m3fn(x / s), rounded to nearest even after saturating to +-448
+ * (x8: [B,H,N,d] bytes, written). Inputs are expected finite: a NaN element
+ * gets a NaN code (0x7F or 0xFF) and is left out of its block's amax (with
+ * rot, every element of its row is NaN after the product and is treated
+ * so). block_rows = 0 runs three launches and uses scales as scratch between
  * them (every entry ends up holding the one scale). */
 FA_API int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, float* scales,
-                 int B, int H, int N, int d, int block_rows, void* stream);
+                 int B, int H, int N, int d, int block_rows, int pow2, void* stream);
 
 /* Forward on fp8 inputs ("FlashAttention v1～v4 完整进化史", v3 part 3: both
  * products on fp8 matrix cores, with block scales): q8, k8, v8 e4m3fn codes
@@ -275,8 +278,11 @@ FA_API int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, floa
  * tile), and the row sum l uses the float32 P~. Both products run on fp8
  * matrix cores into float32 accumulators; the V block scale enters the
  * product with P as the instruction's exponent scale, so sv entries must be
- * powers of two in [2^-126, 2^127] (as fa_quant_fp8 writes them; only their
- * exponent is read). sq and sk must be positive and finite.
+ * powers of two in [2^-126, 2^127] (fa_quant_fp8 with pow2 = 1 writes
+ * them): every 256-row query tile whose key range includes a tile with any
+ * other sv comes out NaN (O and LSE), since the device data is not read
+ * before the launch. sq and sk
+ * (either form) must be positive and finite.
  * o: [B,H,N,d] bf16 (written). lse: [B,H,N] float32 (written). d must be
  * 128. */
 FA_API int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* v8,

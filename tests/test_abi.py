@@ -120,9 +120,10 @@ def test_backward_rejects(lib):
 
 def test_fp8_rejects(lib):
     q = A
-    assert lib.fa_quant_fp8(q, None, A + GAP, A + 2 * GAP, 1, 1, 64, 128, 32, None) == _lib.FA_ERR_UNSUPPORTED
-    assert lib.fa_quant_fp8(q, None, None, A + 2 * GAP, 1, 1, 64, 128, 64, None) == _lib.FA_ERR_INVALID
-    assert lib.fa_quant_fp8(q, None, A + 256, A + 2 * GAP, 1, 1, 64, 128, 64, None) == _lib.FA_ERR_INVALID
+    assert lib.fa_quant_fp8(q, None, A + GAP, A + 2 * GAP, 1, 1, 64, 128, 32, 0, None) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_quant_fp8(q, None, None, A + 2 * GAP, 1, 1, 64, 128, 64, 0, None) == _lib.FA_ERR_INVALID
+    assert lib.fa_quant_fp8(q, None, A + 256, A + 2 * GAP, 1, 1, 64, 128, 64, 0, None) == _lib.FA_ERR_INVALID
+    assert lib.fa_quant_fp8(q, None, A + GAP, A + 2 * GAP, 1, 1, 64, 128, 64, 2, None) == _lib.FA_ERR_INVALID
     s = A + 3 * GAP
     assert lib.fa_fwd_fp8(A, A + GAP, A + 2 * GAP, s, s + GAP, s + 2 * GAP, 64, s + 3 * GAP, s + 4 * GAP,
                           1, 1, 64, 64, 0.125, 0, None) == _lib.FA_ERR_UNSUPPORTED

@@ -1,11 +1,13 @@
 """fp8 path on the GPU ("FlashAttention v1～v4 完整进化史", v3 part 3).
 
 * Quantisation without rotation: codes and scales bit-exact against the
-  oracle's codec (the division x / s is float32 on both sides).
+  oracle's codec (the division x / s is float32 on both sides), for both
+  scale forms (amax / 448, and the power of two at or above it).
 * Quantisation with rotation: the GPU forms x * rot in float32; its codes must
   lie within the codes of the exact product widened by the float32 summation
-  bound, and its scales the powers of two at or above amax / 448 within that
-  bound.
+  bound, and its scales amax / 448 within that bound (or the powers of two at
+  or above it).
+* fp8 attention refuses V scales that are not powers of two (NaN rows).
 * fp8 attention: against the oracle's fp8 emulation on the same codes, element
   by element, within the bound of tests/fp8_bounds.py (the matrix cores' fp8
   accumulation, a few float32 roundings, e4m3 code flips they can cause, and
@@ -67,15 +69,16 @@ def _spread_inputs(w):
     return x
 
 
+@pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("block_rows", [64, 0])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 17, 64, 65, 200, 1000])
-def test_quant_exact(fa, block_rows, d, N):
+def test_quant_exact(fa, block_rows, d, N, pow2):
     w = si.Workload(960 + N, "quant", 2, 3, N, d, "bf16", False, False)
     xt, xv = _bf16_dev(_spread_inputs(w))
-    codes_ref, s_ref, _ = F.quantize(xv, block_rows)
-    announce(f"fa_quant_fp8 block_rows={block_rows} d={d} N={N}")
-    x8, sc = fa.quant_fp8(xt, block_rows=block_rows)
+    codes_ref, s_ref, _ = F.quantize(xv, block_rows, pow2=pow2)
+    announce(f"fa_quant_fp8 block_rows={block_rows} d={d} N={N} pow2={pow2}")
+    x8, sc = fa.quant_fp8(xt, block_rows=block_rows, pow2=pow2)
     _sync()
     got_c, got_s = x8.cpu().numpy(), sc.cpu().numpy()
     assert np.array_equal(got_s.view(np.uint32), s_ref.view(np.uint32)), "scales differ"
@@ -110,10 +113,9 @@ def test_quant_nan_element(fa, rotate):
         assert not np.any((rest & 0x7F) == 0x7F), "NaN codes outside the NaN row"
         y = clean.astype(np.float64) @ rot.astype(np.float64)
         amax = np.abs(np.delete(y[0, 1, 64:128], 70 - 64, axis=0)).max()
-        # the block scale: the power of two at or above amax / 448 (amax of
-        # the float32 product, within 1e-5 of the exact one here)
-        near = {float(F.pow2_scale(np.float32(amax / 448 * f))) for f in (1 - 1e-5, 1 + 1e-5)}
-        assert float(got_s[0, 1, 1]) in near, (got_s[0, 1, 1], amax / 448)
+        # the block scale: amax / 448 of the float32 product, within 1e-5 of
+        # the exact one here
+        assert abs(got_s[0, 1, 1] - amax / 448) <= 1e-5 * amax / 448
     else:
         assert (got_c[0, 1, 70, 5] & 0x7F) == 0x7F, "NaN element not NaN-coded"
         codes_ref, s_ref, _ = F.quantize(clean, 64)
@@ -123,17 +125,18 @@ def test_quant_nan_element(fa, rotate):
         assert np.array_equal(got_c[mask], codes_ref[mask])
 
 
+@pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [17, 200, 1000])
-def test_quant_rotated(fa, d, N):
+def test_quant_rotated(fa, d, N, pow2):
     w = si.Workload(965 + N, "quant-rot", 2, 2, N, d, "bf16", False, False, outlier_frac=0.01,
                     outlier_gain=30.0, rotate=True)
     x = si.make_inputs(w, names=("q",))
     xt, xv = _bf16_dev(x["q"])
     rot = x["rot"]
     import torch
-    announce(f"fa_quant_fp8 rotated d={d} N={N}")
-    x8, sc = fa.quant_fp8(xt, rot=_to_dev(rot, torch.float32), block_rows=64)
+    announce(f"fa_quant_fp8 rotated d={d} N={N} pow2={pow2}")
+    x8, sc = fa.quant_fp8(xt, rot=_to_dev(rot, torch.float32), block_rows=64, pow2=pow2)
     _sync()
     got_c, got_s = x8.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
     x64 = xv.astype(np.float64)
@@ -154,11 +157,14 @@ def test_quant_rotated(fa, d, N):
                 e = err[b, h, blk].max()
                 lo = (amax - e) / 448 * (1 - u)
                 hi = (amax + e) / 448 * (1 + u)
-                # float32 amax / 448 lies in [lo, hi]; its scale is the power
-                # of two at or above it
-                s_lo, s_hi = (float(F.pow2_scale(np.float32(x))) for x in (lo, hi))
-                assert s_lo <= got_s[b, h, i] <= s_hi and np.frexp(got_s[b, h, i])[0] == 0.5, \
-                    (b, h, i, got_s[b, h, i], amax / 448)
+                # float32 amax / 448 lies in [lo, hi] (with pow2, its scale is
+                # the power of two at or above it)
+                if pow2:
+                    s_lo, s_hi = (float(F.pow2_scale(np.float32(x))) for x in (lo, hi))
+                    assert s_lo <= got_s[b, h, i] <= s_hi and np.frexp(got_s[b, h, i])[0] == 0.5, \
+                        (b, h, i, got_s[b, h, i], amax / 448)
+                else:
+                    assert lo <= got_s[b, h, i] <= hi, (b, h, i, got_s[b, h, i], amax / 448)
     srow = np.repeat(got_s, 64, axis=2)[:, :, :N, None]
     qlo = (y - err) / srow * (1 - 2 * u)
     qhi = (y + err) / srow * (1 + 2 * u)
@@ -167,14 +173,14 @@ def test_quant_rotated(fa, d, N):
     got_v = F.e4m3_decode(got_c)
     ok = (got_v >= lo_v) & (got_v <= hi_v)
     assert ok.all(), f"{np.sum(~ok)} codes outside the float32-summation range"
-    ref_c, _, _ = F.quantize(xv, 64, rot)
-    print(f"rotated d={d} N={N}: {np.sum(got_c != ref_c)} of {got_c.size} codes differ from the float64 product's")
+    ref_c, _, _ = F.quantize(xv, 64, rot, pow2=pow2)
+    print(f"rotated d={d} N={N} pow2={pow2}: {np.sum(got_c != ref_c)} of {got_c.size} codes differ from the float64 product's")
 
 
 def _fp8_codes(x, rot):
     q8, sq, _ = F.quantize(x["q"], 64, rot)
     k8, sk, _ = F.quantize(x["k"], 64, rot)
-    v8, sv, _ = F.quantize(x["v"], 64)
+    v8, sv, _ = F.quantize(x["v"], 64, pow2=True)
     return q8, sq, k8, sk, v8, sv
 
 
@@ -232,6 +238,25 @@ def test_fwd_fp8_zero_scale(fa, causal):
     assert worst[0] <= 1.0 and worst[1] <= 1.0, worst
 
 
+def test_fwd_fp8_refuses_non_power_of_two_v_scale(fa):
+    """A V scale that is not a power of two turns the rows that use its tile
+    into NaN (O and LSE); rows that never reach the tile are unaffected."""
+    import torch
+    N = 200
+    w = si.Workload(991, "fp8 bad sv", 1, 2, N, 128, "bf16", True, False)
+    x = si.make_inputs(w, names=("q", "k", "v"))
+    codes = list(_fp8_codes(x, None))
+    sv = codes[5].copy()
+    sv[0, 1, 2] *= np.float32(1.5)           # head 1, keys 128..191
+    codes[5] = sv
+    announce("fa_fwd_fp8 non-power-of-two V scale, causal")
+    o, lse = _run_fwd_fp8(fa, codes, w.scale, True)
+    assert np.all(np.isfinite(o[0, 0])) and np.all(np.isfinite(lse[0, 0]))
+    # causal: 256-row workgroups see tile 2 only from query 128 on, but the
+    # flag is per workgroup, so every row of the workgroup that reads it is NaN
+    assert np.all(np.isnan(o[0, 1])) and np.all(np.isnan(lse[0, 1]))
+
+
 @pytest.fixture(scope="module")
 def workload5(fa):
     """GPU outputs of the fp8 workload, both quantisation schemes, plus the inputs."""
@@ -245,7 +270,7 @@ def workload5(fa):
         announce(f"workload 5: fa_quant_fp8 block_rows={br} rot={use_rot}")
         q8, sq = fa.quant_fp8(dev["q"], rot=rot if use_rot else None, block_rows=br)
         k8, sk = fa.quant_fp8(dev["k"], rot=rot if use_rot else None, block_rows=br)
-        v8, sv = fa.quant_fp8(dev["v"], block_rows=br)
+        v8, sv = fa.quant_fp8(dev["v"], block_rows=br, pow2=True)
         announce(f"workload 5: fa_fwd_fp8 ({name})")
         o, lse = fa.fwd_fp8(q8, k8, v8, sq, sk, sv, causal=False, scale=w.scale, block_rows=br)
         _sync()
@@ -288,7 +313,7 @@ def test_workload5_per_tensor_matches_emulation_rmse(workload5):
     codes = []
     for n in "qkv":
         # one scale for the whole tensor; the codes of the sampled head only
-        s = F.block_scales(x[n], 0)[b:b + 1, h:h + 1]
+        s = F.block_scales(x[n], 0, pow2=(n == "v"))[b:b + 1, h:h + 1]
         c = F.e4m3_encode((x[n][b:b + 1, h:h + 1].astype(np.float32) / s[0, 0, 0]).astype(np.float32))
         codes += [c, s]
     o_em, _ = F.fp8_attention_tiled(*codes, w.scale, False)
