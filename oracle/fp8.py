@@ -42,6 +42,13 @@ The tiled fp8 attention emulation follows the pages' steps (it is an
 approximation, not a closed form); its pins are that with P left in float64 it
 reduces to the exact oracle on the dequantised inputs, and that its per-tile P
 rounding stays within the e4m3 half-step bound.
+
+The backward of the fp8 forward is not described on the pages (they put fp8
+in the forward only). Reading: the codes and scales are the inputs, so no
+gradient flows through the rounding; the gradients are those of attention at
+the dequantised Q, K, V, formed by the backward step of "6.1 FlashAttention
+V1详解" (sections 6.1-6.2) from the fp8 forward's saved O and L. Pinned: with
+the exact O and L of the dequantised inputs it is the exact backward.
 """
 
 from __future__ import annotations
@@ -49,7 +56,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "pow2_scale", "block_scales",
-           "quantize", "dequantize", "fp8_attention_tiled"]
+           "quantize", "dequantize", "fp8_attention_tiled", "fp8_backward"]
 
 E4M3_MAX = 448.0
 _MIN_NORMAL_EXP = -6          # 2^-6 is the smallest normal magnitude
@@ -235,3 +242,17 @@ def fp8_attention_tiled(q8, sq, k8, sk, v8, sv, scale: float, causal: bool,
             o_all[b, h] = o / np.where(l > 0, l, 1.0)[:, None]
             lse_all[b, h] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
     return o_all, lse_all
+
+
+def fp8_backward(q8, sq, k8, sk, v8, sv, o, lse, do, scale: float, causal: bool, block_rows: int = 64):
+    """Gradients (dQ, dK, dV, float64) with respect to the dequantised Q, K, V
+    of the fp8 forward, from its saved O [B, H, N, d] and LSE [B, H, N] and
+    the upstream gradient dO: the backward step on the saved statistics
+    (P = exp(S - L) from the exact scores of the dequantised inputs, D =
+    rowsum(dO * O)), applied to decode(code) * s.
+    """
+    from oracle import attention as A
+    qd = dequantize(q8, sq, block_rows)
+    kd = dequantize(k8, sk, block_rows)
+    vd = dequantize(v8, sv, block_rows)
+    return A.backward_from_saved(qd, kd, vd, o, lse, do, scale, causal)

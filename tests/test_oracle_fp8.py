@@ -224,3 +224,47 @@ def test_bound_helper_rebuilds_the_emulation():
                                       qc["v"][0][0, 0], qc["v"][1][0, 0], 0.25, causal, rows)
         assert np.max(np.abs(o_em - o[0, 0])) <= 1e-12
         assert np.max(np.abs(l_em - lse[0, 0])) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_backward_with_exact_statistics_is_the_exact_backward(causal):
+    """Given the exact O and L of the dequantised inputs, the fp8 backward is
+    the exact backward of attention at those inputs (A.backward recomputes
+    everything itself, blockwise, and shares no step with the saved-statistics
+    path but the definitions)."""
+    rng = np.random.default_rng(38)
+    x = {n: rng.standard_normal((1, 2, 150, 16)) for n in "qkv"}
+    x["k"][:, :, 70:80] *= 6.0
+    do = rng.standard_normal((1, 2, 150, 16))
+    qc = {n: F.quantize(x[n], 64, pow2=True) for n in "qkv"}
+    deq = {n: F.dequantize(qc[n][0], qc[n][1], 64) for n in "qkv"}
+    o, lse = A.forward(deq["q"], deq["k"], deq["v"], 0.25, causal)
+    got = F.fp8_backward(qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1], qc["v"][0], qc["v"][1],
+                         o, lse, do, 0.25, causal)
+    ref = A.backward(deq["q"], deq["k"], deq["v"], do, 0.25, causal)
+    for g, r in zip(got, ref):
+        assert np.max(np.abs(g - r)) <= 1e-10 * max(1.0, np.max(np.abs(r)))
+
+
+def test_fp8_backward_follows_the_saved_output():
+    """D = rowsum(dO * O) uses the given O: moving O by e along dO moves dQ
+    and dK by exactly the linear term and leaves dV alone."""
+    rng = np.random.default_rng(39)
+    x = {n: rng.standard_normal((1, 1, 96, 8)) for n in "qkv"}
+    do = rng.standard_normal((1, 1, 96, 8))
+    qc = {n: F.quantize(x[n], 64, pow2=True) for n in "qkv"}
+    deq = {n: F.dequantize(qc[n][0], qc[n][1], 64) for n in "qkv"}
+    o, lse = A.forward(deq["q"], deq["k"], deq["v"], 0.3, False)
+    args = (qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1], qc["v"][0], qc["v"][1])
+    g0 = F.fp8_backward(*args, o, lse, do, 0.3, False)
+    e = 1e-3
+    g1 = F.fp8_backward(*args, o + e * do, lse, do, 0.3, False)
+    assert np.array_equal(g0[2], g1[2])
+    # D grows by e * rowsum(dO^2); dS by -P * that; dQ by -scale * e * (P * rowsum) K
+    s = 0.3 * deq["q"][0, 0] @ deq["k"][0, 0].T
+    p = np.exp(s - lse[0, 0][:, None])
+    r = np.sum(do[0, 0] ** 2, axis=1)
+    ddq = -0.3 * e * (p * r[:, None]) @ deq["k"][0, 0]
+    ddk = -0.3 * e * (p * r[:, None]).T @ deq["q"][0, 0]
+    assert np.max(np.abs((g1[0] - g0[0])[0, 0] - ddq)) <= 1e-12
+    assert np.max(np.abs((g1[1] - g0[1])[0, 0] - ddk)) <= 1e-12
