@@ -273,6 +273,35 @@ def fp8_section(fa, steps: int, warmup: int):
     q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     f_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     tf = attention_flops(B, H, N, d, False) / (f_ms * 1e-3) / 1e12
+
+    # The backward of the fp8 forward (fa_bwd_fp8: Q, K, V decoded exactly
+    # into bf16, then the bf16 backward), on all-power-of-two quantisation as
+    # it requires; dO seeded N(0, 1).
+    q8, sq = fa.quant_fp8(x["q"], rot=rot, pow2=True)
+    k8, sk = fa.quant_fp8(x["k"], rot=rot, pow2=True)
+    v8, sv = fa.quant_fp8(x["v"], pow2=True)
+    del x
+    o, lse = fa.fwd_fp8(q8, k8, v8, sq, sk, sv, causal=False, scale=w.scale)
+    do = torch.randn((B, H, N, d), device="cuda", generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    ws = torch.empty(fa.bwd_fp8_workspace_bytes(B, H, N, d), device="cuda", dtype=torch.uint8)
+    grads = [torch.empty_like(o) for _ in range(3)]
+
+    def run_bwd():
+        fa.bwd_fp8(q8, k8, v8, sq, sk, sv, o, lse, do, causal=False, scale=w.scale, workspace=ws,
+                   dq=grads[0], dk=grads[1], dv=grads[2])
+
+    for _ in range(warmup):
+        run_bwd()
+    torch.cuda.synchronize()
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evb:
+        e[0].record()
+        run_bwd()
+        e[1].record()
+    torch.cuda.synchronize()
+    b_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evb]))
+    b_tf = attention_flops(B, H, N, d, False, True) / (b_ms * 1e-3) / 1e12
+    del ws, grads, do, o, lse
     # Quantiser: algorithmic HBM bytes of the three launches (2 B read and 1 B
     # written per element, plus the block scales).
     q_bytes = 3 * (B * H * N * d * 3 + B * H * (-(-N // 64)) * 4)
@@ -282,7 +311,10 @@ def fp8_section(fa, steps: int, warmup: int):
             "quant_frac_of_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4),
             "fwd_ms": round(f_ms, 4), "fwd_tflops": round(tf, 2),
             "fwd_frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
-            "fwd_at_clock": at_clock(tf, PEAK_FP8_TFLOPS, "attn_fwd_fp8_d128_N8192_B4_H32", ["fa_fp8.hip", "fa_device.h"])}
+            "fwd_at_clock": at_clock(tf, PEAK_FP8_TFLOPS, "attn_fwd_fp8_d128_N8192_B4_H32", ["fa_fp8.hip", "fa_device.h"]),
+            "bwd_ms": round(b_ms, 4), "bwd_tflops": round(b_tf, 2),
+            "bwd_frac_of_bf16_peak": round(b_tf / PEAK_BF16_TFLOPS, 4),
+            "bwd_note": "fa_bwd_fp8 (exact bf16 decoding of Q, K, V + the bf16 backward), power-of-two scales"}
 
 
 def det_section(fa, q, k, v, o, lse, do, causal: bool, steps: int, warmup: int, bwd_ms: float):

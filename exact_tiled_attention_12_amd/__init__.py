@@ -12,7 +12,8 @@ from ._lib import FAError, LIB_PATH, load  # noqa: F401
 
 def __getattr__(name):
     if name in ("fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "bwd_det_workspace_bytes",
-                "bwd_gqa_workspace_bytes", "fwd_varlen", "bwd_varlen", "quant_fp8", "fwd_fp8"):
+                "bwd_gqa_workspace_bytes", "fwd_varlen", "bwd_varlen", "quant_fp8", "fwd_fp8", "dequant_fp8",
+                "bwd_fp8", "bwd_fp8_workspace_bytes"):
         from . import api
         return getattr(api, name)
     raise AttributeError(name)

@@ -49,6 +49,10 @@ SIGNATURES = {
     "fa_quant_fp8": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),
     "fa_fwd_fp8": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _p, _p,
                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
+    "fa_dequant_fp8": (_c_int, [_p, _p, _c_int, _p, _c_int, _c_int, _c_int, _c_int, _p]),
+    "fa_bwd_fp8_workspace_bytes": (ctypes.c_size_t, [_c_int, _c_int, _c_int, _c_int]),
+    "fa_bwd_fp8": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t,
+                            _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _p]),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
     "fa_last_error": (ctypes.c_char_p, []),
 }

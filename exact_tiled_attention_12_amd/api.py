@@ -13,7 +13,7 @@ import torch
 from . import _lib
 
 __all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "bwd_det_workspace_bytes", "bwd_gqa_workspace_bytes",
-           "fwd_varlen", "bwd_varlen", "quant_fp8", "fwd_fp8"]
+           "fwd_varlen", "bwd_varlen", "quant_fp8", "fwd_fp8", "dequant_fp8", "bwd_fp8", "bwd_fp8_workspace_bytes"]
 
 
 def _stream(t: torch.Tensor):
@@ -307,3 +307,52 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, causal: bool = False, scale: float | None = 
                                 int(bool(causal)), _stream(q8))
     _lib.check(st, "fa_fwd_fp8")
     return out, lse
+
+
+def dequant_fp8(x8, scales, block_rows: int = 64, out=None):
+    """bf16 values decode(x8) * s (exact for power-of-two scales; NaN blocks
+    where a scale is not a power of two)."""
+    B, H, N, d = _shape4(x8)
+    _check_tensor(x8, "x8", torch.uint8, (B, H, N, d))
+    _check_tensor(scales, "scales", torch.float32, (B, H, (N + 63) // 64))
+    out = torch.empty((B, H, N, d), device=x8.device, dtype=torch.bfloat16) if out is None else out
+    _check_tensor(out, "out", torch.bfloat16, (B, H, N, d))
+    st = _lib.load().fa_dequant_fp8(x8.data_ptr(), scales.data_ptr(), int(block_rows), out.data_ptr(),
+                                    B, H, N, d, _stream(x8))
+    _lib.check(st, "fa_dequant_fp8")
+    return out
+
+
+def bwd_fp8_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.load().fa_bwd_fp8_workspace_bytes(B, H, N, d))
+
+
+def bwd_fp8(q8, k8, v8, sq, sk, sv, o, lse, do, causal: bool = False, scale: float | None = None,
+            block_rows: int = 64, workspace=None, dq=None, dk=None, dv=None):
+    """dQ, dK, dV (bf16) with respect to the dequantised inputs of fwd_fp8,
+    from its o and lse; all three tensors quantised with pow2=True."""
+    B, H, N, d = _shape4(q8)
+    nb = (N + 63) // 64
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _check_tensor(t, n, torch.uint8, (B, H, N, d))
+    for t, n in ((sq, "sq"), (sk, "sk"), (sv, "sv")):
+        _check_tensor(t, n, torch.float32, (B, H, nb))
+    for t, n in ((o, "o"), (do, "do")):
+        _check_tensor(t, n, torch.bfloat16, (B, H, N, d))
+    _check_tensor(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = torch.empty(bwd_fp8_workspace_bytes(B, H, N, d), device=q8.device, dtype=torch.uint8)
+    dq = torch.empty_like(o) if dq is None else dq
+    dk = torch.empty_like(o) if dk is None else dk
+    dv = torch.empty_like(o) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_tensor(t, n, torch.bfloat16, (B, H, N, d))
+    st = _lib.load().fa_bwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), sq.data_ptr(), sk.data_ptr(),
+                                sv.data_ptr(), int(block_rows), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), B, H, N, d, float(scale),
+                                int(bool(causal)), _stream(q8))
+    _lib.check(st, "fa_bwd_fp8")
+    return dq, dk, dv

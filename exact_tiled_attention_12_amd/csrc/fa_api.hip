@@ -409,6 +409,67 @@ int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, float* scal
   return launched(fa::launch_quant_fp8(d, a, B, H, (hipStream_t)stream), "fp8 quantisation");
 }
 
+int fa_dequant_fp8(const unsigned char* x8, const float* scales, int block_rows, void* out, int B, int H, int N,
+                   int d, void* stream) {
+  int rc = check_shape(B, H, N, d, 1.f);
+  if (rc) return rc;
+  if (block_rows != 64 && block_rows != 0)
+    return fail(FA_ERR_UNSUPPORTED, "block_rows must be 64 or 0 (got %d)", block_rows);
+  const size_t n = (size_t)B * H * N * d;
+  const size_t sb = (size_t)B * H * ((N + 63) / 64) * 4;
+  const Buf in[2] = {{x8, n, "x8", 16}, {scales, sb, "scales", 4}};
+  const Buf out_[1] = {{out, n * 2, "out", 16}};
+  rc = check_bufs(in, 2, out_, 1);
+  if (rc) return rc;
+  return launched(fa::launch_dequant_fp8(x8, scales, out, B, H, N, d, (hipStream_t)stream), "fp8 decoding");
+}
+
+size_t fa_bwd_fp8_workspace_bytes(int B, int H, int N, int d) {
+  const size_t base = fa_bwd_workspace_bytes(B, H, N, d);
+  if (base == 0) return 0;
+  // the bf16 backward's workspace, then the decoded Q, K and V (bf16)
+  return base + 3 * align256((size_t)B * H * N * d * 2);
+}
+
+int fa_bwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* v8, const float* sq,
+               const float* sk, const float* sv, int block_rows, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+  int rc = check_shape(B, H, N, d, scale);
+  if (rc) return rc;
+  if (block_rows != 64 && block_rows != 0)
+    return fail(FA_ERR_UNSUPPORTED, "block_rows must be 64 or 0 (got %d)", block_rows);
+  const size_t need = fa_bwd_fp8_workspace_bytes(B, H, N, d);
+  if (workspace == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(FA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID, "workspace has %zu bytes, needs fa_bwd_fp8_workspace_bytes() = %zu",
+                workspace_bytes, need);
+  const size_t n = (size_t)B * H * N * d;
+  const size_t sb = (size_t)B * H * ((N + 63) / 64) * 4;
+  const size_t lb = (size_t)B * H * N * 4;
+  const Buf in[9] = {{q8, n, "q8", 16},  {k8, n, "k8", 16},   {v8, n, "v8", 16},
+                     {sq, sb, "sq", 4},  {sk, sb, "sk", 4},   {sv, sb, "sv", 4},
+                     {o, n * 2, "o", 16}, {lse, lb, "lse", 4}, {dout, n * 2, "dout", 16}};
+  const Buf out[4] = {{dq, n * 2, "dq", 16}, {dk, n * 2, "dk", 16}, {dv, n * 2, "dv", 16},
+                      {workspace, need, "workspace", 256}};
+  rc = check_bufs(in, 9, out, 4);
+  if (rc) return rc;
+  // Decoded Q, K, V after the bf16 backward's own workspace.
+  const size_t base = fa_bwd_workspace_bytes(B, H, N, d);
+  const size_t tb = align256(n * 2);
+  char* dec = (char*)workspace + base;
+  const hipStream_t st = (hipStream_t)stream;
+  const unsigned char* codes[3] = {q8, k8, v8};
+  const float* scales[3] = {sq, sk, sv};
+  for (int t = 0; t < 3; ++t) {
+    rc = launched(fa::launch_dequant_fp8(codes[t], scales[t], dec + t * tb, B, H, N, d, st), "fp8 decoding");
+    if (rc) return rc;
+  }
+  return bwd_common(fa::DType::BF16, dec, dec + tb, dec + 2 * tb, o, lse, dout, dq, dk, dv, workspace, base, B, H,
+                    N, d, scale, causal, stream);
+}
+
 int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* v8, const float* sq,
                const float* sk, const float* sv, int block_rows, void* o, float* lse, int B, int H, int N, int d,
                float scale, int causal, void* stream) {

@@ -30,6 +30,7 @@
 //     matrix instruction's 8-bit exponent scale of the V operand, so the
 //     accumulator stays in the units of O; it is multiplied by alpha only in
 //     steps where some row's maximum moved, and O = acc / l at the end.
+#include <algorithm>
 #include <cfloat>
 #include <type_traits>
 
@@ -303,6 +304,39 @@ hipError_t launch_quant_d(const QuantArgs& a, int B, int H, hipStream_t st) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((quant_kernel<D, ROT, kGivenScale>), dim3(grid), dim3(kQThreads), 0, st, a, nb, total);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- decoding
+
+// out = decode(code) * s of the code's 64-row block, rounded to bf16, 16
+// codes per thread. The e4m3 decode and, for a power-of-two s, the product
+// are exact; so is the bf16 value while it stays inside bf16's range. A
+// block whose scale is not a power of two in [2^-126, 2^127] is written as
+// NaN: the backward built on these values requires exact ones.
+__global__ __launch_bounds__(256) void dequant_kernel(const unsigned char* x8, const float* scales, __bf16* out,
+                                                      int N, int d, int nb64, int bh0) {
+  // grid: x covers one (batch, head) in 16-code chunks, y the (batch, head)
+  const unsigned per_head16 = (unsigned)N * (unsigned)d / 16u;
+  const unsigned i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= per_head16) return;
+  const size_t bh = (size_t)bh0 + blockIdx.y;
+  const unsigned row = i * 16u / (unsigned)d;
+  const float s = scales[bh * nb64 + row / 64u];
+  const uint32_t sb = __float_as_uint(s), e8 = (sb >> 23) & 0xFFu;
+  const bool bad = (sb & 0x807FFFFFu) != 0u || e8 == 0u || e8 == 255u;
+  const size_t e0 = bh * N * d + (size_t)i * 16u;
+  const u32x4 c = *(const u32x4*)(x8 + e0);
+  const float nan = __builtin_nanf("");
+  u32x4 w[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[k], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[k], true);
+    w[k >> 1][2 * (k & 1)] = pack_bf16x2(bad ? nan : lo[0] * s, bad ? nan : lo[1] * s);
+    w[k >> 1][2 * (k & 1) + 1] = pack_bf16x2(bad ? nan : hi[0] * s, bad ? nan : hi[1] * s);
+  }
+  *(u32x4*)(out + e0) = w[0];
+  *(u32x4*)(out + e0 + 8) = w[1];
 }
 
 // ---------------------------------------------------------------- attention
@@ -782,6 +816,21 @@ hipError_t launch_attn(const Fp8FwdArgs& a, int grid, hipStream_t s) {
 hipError_t launch_quant_fp8(int d, QuantArgs a, int B, int H, hipStream_t s) {
   if (d == 64) return a.rot ? launch_quant_d<64, true>(a, B, H, s) : launch_quant_d<64, false>(a, B, H, s);
   return a.rot ? launch_quant_d<128, true>(a, B, H, s) : launch_quant_d<128, false>(a, B, H, s);
+}
+
+hipError_t launch_dequant_fp8(const unsigned char* x8, const float* scales, void* out, int B, int H, int N, int d,
+                              hipStream_t s) {
+  const unsigned per_head16 = (unsigned)N * (unsigned)d / 16u;
+  const unsigned gx = (per_head16 + 255u) / 256u;
+  const int nbh = B * H;
+  for (int bh0 = 0; bh0 < nbh; bh0 += 65535) {
+    const int gy = std::min(65535, nbh - bh0);
+    hipLaunchKernelGGL(dequant_kernel, dim3(gx, (unsigned)gy), dim3(256), 0, s, x8, scales, (__bf16*)out, N, d,
+                       (N + 63) / 64, bh0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_fwd_fp8(int d, int causal, Fp8FwdArgs a, int B, int H, hipStream_t s) {

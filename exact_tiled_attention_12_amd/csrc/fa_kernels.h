@@ -108,5 +108,7 @@ hipError_t launch_bwd(DType dt, int d, int causal, BwdArgs a, int B, int H, int 
 hipError_t launch_bwd_bf16_main(int d, int causal, BwdArgs a, int B, int H, hipStream_t s);
 hipError_t launch_quant_fp8(int d, QuantArgs a, int B, int H, hipStream_t s);
 hipError_t launch_fwd_fp8(int d, int causal, Fp8FwdArgs a, int B, int H, hipStream_t s);
+hipError_t launch_dequant_fp8(const unsigned char* x8, const float* scales, void* out, int B, int H, int N, int d,
+                              hipStream_t s);
 
 }  // namespace fa

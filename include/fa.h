@@ -290,6 +290,42 @@ FA_API int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const un
                void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, void* stream);
 
+/* Decoding of fp8 codes: out = decode(x8) * s of the code's 64-row block
+ * (x8, scales as fa_quant_fp8 writes them with the same block_rows, 64 or
+ * 0), rounded to bf16; out: [B,H,N,d] bf16 (written). Exact when s is a
+ * power of two and the product stays in bf16's range. A block whose scale is
+ * not a power of two in [2^-126, 2^127] is written as NaN (the device data
+ * is not read before the launch). */
+FA_API int fa_dequant_fp8(const unsigned char* x8, const float* scales, int block_rows, void* out,
+                   int B, int H, int N, int d, void* stream);
+
+/* Workspace bytes fa_bwd_fp8 needs: fa_bwd_workspace_bytes plus three
+ * decoded [B,H,N,d] bf16 tensors (each 256-byte aligned); 0 for invalid
+ * sizes. */
+FA_API size_t fa_bwd_fp8_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward of the fp8 forward. The pages put fp8 in the forward only
+ * ("FlashAttention v1～v4 完整进化史", v3 part 3); this library's reading:
+ * the codes and scales are the inputs, so no gradient flows through the
+ * rounding, and dq, dk, dv are the gradients with respect to the dequantised
+ * Q, K, V, formed by the backward step of "6.1 FlashAttention V1详解"
+ * (sections 6.1-6.2) from fa_fwd_fp8's saved o and lse: P = exp(S - L) with
+ * the scores of the dequantised inputs, D = rowsum(dout * o). All three
+ * tensors must be quantised with power-of-two scales (fa_quant_fp8 with
+ * pow2 = 1): the call decodes them into bf16 in the workspace, exactly for
+ * such scales, and runs the bf16 backward (fa_bwd) on them; a block with any
+ * other scale decodes to NaN and so do the gradients it reaches.
+ * q8, k8, v8: [B,H,N,d] codes; sq, sk, sv: [B,H,ceil(N/64)] scales with
+ * block_rows 64 or 0; o: [B,H,N,d] bf16 and lse: [B,H,N] float32 from
+ * fa_fwd_fp8; dout: [B,H,N,d] bf16; dq, dk, dv: [B,H,N,d] bf16 (written);
+ * workspace: >= fa_bwd_fp8_workspace_bytes bytes, 256-byte aligned,
+ * overwritten. d must be 64 or 128. */
+FA_API int fa_bwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* v8,
+               const float* sq, const float* sk, const float* sv, int block_rows,
+               const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
 /* Static text for a status code. */
 FA_API const char* fa_status_string(int status);
 

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -134,6 +134,37 @@ def test_fp8_rejects(lib):
         assert lib.fa_fwd_fp8(A, A + GAP, A + 2 * GAP, s, s + GAP, s + 2 * GAP, br, s + 3 * GAP, s + 4 * GAP,
                               1, 1, 64, 128, 0.125, 0, None) == _lib.FA_ERR_UNSUPPORTED
         assert "block_rows" in lib.fa_last_error().decode()
+        assert lib.fa_dequant_fp8(A, s, br, A + GAP, 1, 1, 64, 128, None) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_dequant_fp8(A, s, 64, A + 8, 1, 1, 64, 128, None) == _lib.FA_ERR_UNSUPPORTED   # misaligned
+    assert lib.fa_dequant_fp8(A, s, 64, A + 256, 1, 1, 64, 128, None) == _lib.FA_ERR_INVALID     # overlap
+    assert lib.fa_dequant_fp8(A, None, 64, A + GAP, 1, 1, 64, 128, None) == _lib.FA_ERR_INVALID
+
+
+def _bwd_fp8(lib, ws=A + 20 * GAP, ws_bytes=None, B=1, H=1, N=64, d=128, block_rows=64, **over):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_fp8_workspace_bytes(B, H, N, d)
+    p = {n: A + i * GAP for i, n in enumerate(("q8", "k8", "v8", "sq", "sk", "sv", "o", "lse", "do",
+                                                 "dq", "dk", "dv"))}
+    p.update(over)
+    return lib.fa_bwd_fp8(p["q8"], p["k8"], p["v8"], p["sq"], p["sk"], p["sv"], block_rows, p["o"], p["lse"],
+                          p["do"], p["dq"], p["dk"], p["dv"], ws, ws_bytes, B, H, N, d, 0.125, 1, None)
+
+
+def test_fp8_backward_rejects_and_workspace(lib):
+    B, H, N, d = 2, 3, 100, 128
+    base = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    tb = -(-(B * H * N * d * 2) // 256) * 256
+    assert lib.fa_bwd_fp8_workspace_bytes(B, H, N, d) == base + 3 * tb
+    assert lib.fa_bwd_fp8_workspace_bytes(0, H, N, d) == 0
+    assert _bwd_fp8(lib, ws=None) == _lib.FA_ERR_INVALID
+    assert _bwd_fp8(lib, ws_bytes=100) == _lib.FA_ERR_INVALID
+    assert _bwd_fp8(lib, ws=A + 20 * GAP + 16) == _lib.FA_ERR_UNSUPPORTED
+    assert _bwd_fp8(lib, block_rows=32) == _lib.FA_ERR_UNSUPPORTED
+    assert _bwd_fp8(lib, d=32) == _lib.FA_ERR_UNSUPPORTED
+    assert _bwd_fp8(lib, dq=A + 256) == _lib.FA_ERR_INVALID          # dq overlaps q8
+    assert _bwd_fp8(lib, dk=A + 9 * GAP) == _lib.FA_ERR_INVALID      # dk aliases dq
+    assert _bwd_fp8(lib, sv=None) == _lib.FA_ERR_INVALID
+    assert lib.fa_last_error()
 
 
 def test_det_workspace_is_linear_in_n(lib):
