@@ -140,20 +140,45 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  int wg = blockIdx.x;
+  // Work items are (batch or sequence, head, query tile). With more items
+  // than CUs and the (batch, head) pairs a multiple of 8, the launch is
+  // persistent: one workgroup per CU, and the workgroups of XCD x (ids go to
+  // the XCDs round-robin) take the items 8 m + x of that XCD, round by round
+  // in snake order (round r: m = r S + j, or r S + S - 1 - j when r is odd,
+  // for the XCD's S workgroups j), so that with items in decreasing order of
+  // work every workgroup gets about the same total; a workgroup then starts
+  // its next item without a new launch. Otherwise one item per workgroup.
+  for (int round = 0;; ++round) {
+  int wg, nsh;   // item, (batch or sequence, head) pairs
+  if (!VARLEN && a.persist) {
+    const int S = (int)gridDim.x >> 3, x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
+    const int m = round * S + ((round & 1) ? S - 1 - j : j);
+    wg = 8 * m + x;
+    if (wg >= a.n_items) break;
+    nsh = a.n_items / a.n_qtiles;
+  } else {
+    if (round > 0) break;
+    wg = blockIdx.x;
+    nsh = gridDim.x / a.n_qtiles;
+  }
   int bh, t;
   // Causal or packed variable-length, with the (batch or sequence, head)
-  // pairs a multiple of 8: each pair stays on one XCD (workgroups go to XCDs
-  // round-robin by id) and every XCD runs its pairs' tiles tile-major, the
-  // heaviest tiles (the last ones, of the longest sequences) first.
-  // Otherwise the tiles of one pair are grouped on one XCD and run in order
-  // (causal: heaviest first); with equal tiles that keeps a head's K/V in L2.
-  const int nsh = gridDim.x / a.n_qtiles;        // (batch or sequence, head) pairs
+  // pairs a multiple of 8: each pair stays on one XCD and every XCD runs its
+  // pairs' tiles tile-major, the heaviest tiles (the last ones, of the
+  // longest sequences) first. Otherwise the tiles of one pair are grouped on
+  // one XCD and run in order (causal: heaviest first); with equal tiles that
+  // keeps a head's K/V in L2.
   if ((CAUSAL || VARLEN) && a.remap && (nsh & 7) == 0) {
     const int x = wg & 7, j = wg >> 3;           // XCD, position within it
     const int per = nsh >> 3;
     t = j / per;
     bh = (j - t * per) * 8 + x;
+  } else if (!VARLEN && a.persist) {
+    // equal tiles: the XCD's heads one after the other
+    const int x = wg & 7, m = wg >> 3;
+    const int hx = m / a.n_qtiles;
+    bh = hx * 8 + x;
+    t = m - hx * a.n_qtiles;
   } else {
     if (a.remap) wg = xcd_remap(wg, gridDim.x);
     bh = wg / a.n_qtiles;   // (batch, head), or (sequence, head) for VARLEN
@@ -172,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     s0 = min(max(s0, 0), a.N);
     s1 = min(max(s1, s0), a.N);
     N = min(s1 - s0, a.n_qtiles * kBR);
-    if (qt * kBR >= N) return;   // uniform: the tile lies past the sequence
+    if (qt * kBR >= N) continue;   // uniform: the tile lies past the sequence
     const int kvh = h / a.group;
     base = ((size_t)h * a.N + s0) * D;
     kv_base = ((size_t)kvh * a.N + s0) * D;
@@ -486,7 +511,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
       }
     if (hh == 0) a.lse[lse_base + qrow] = lt == 0.f ? -INFINITY : (m_ref + fast_log2(lt)) * kLn2;
   }
+  // Every wave is done with the ring before the next item's tiles land in it.
+  ring_barrier();
+  }
 #endif
+}
+
+// Compute units of the current device (0 if it cannot be read), looked up
+// once per device.
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <int D, bool CAUSAL>
@@ -508,8 +550,17 @@ hipError_t launch_fwd_bf16(int d, int causal, FwdArgs a, int B, int H, hipStream
   // Packed variable-length batch: B sequences, tiles of the longest; one
   // workgroup per (sequence, head, tile).
   a.n_qtiles = ((a.cu_seqlens != nullptr ? a.max_seqlen : a.N) + kBR - 1) / kBR;
-  const long long grid = (long long)B * H * a.n_qtiles;
+  long long grid = (long long)B * H * a.n_qtiles;
   a.remap = (grid % 8 == 0) ? 1 : 0;
+  // Persistent launch: one workgroup per CU (a multiple of 8, one per XCD
+  // slot), when there are more items than that.
+  a.n_items = (int)grid;
+  a.persist = 0;
+  const int n_cu = cu_count() & ~7;
+  if (a.cu_seqlens == nullptr && ((long long)B * H) % 8 == 0 && n_cu >= 8 && grid > n_cu) {
+    a.persist = 1;
+    grid = n_cu;
+  }
   if (d == 64) return causal ? launch<64, true>(a, (int)grid, s) : launch<64, false>(a, (int)grid, s);
   return causal ? launch<128, true>(a, (int)grid, s) : launch<128, false>(a, (int)grid, s);
 }

@@ -25,6 +25,8 @@ struct FwdArgs {
   // a head) and n_qtiles the tiles of the longest sequence.
   const int* cu_seqlens;
   int max_seqlen;
+  int n_items;    // filled by the launcher: work items (batch or sequence, head, query tile)
+  int persist;    // filled by the launcher: 1 if workgroups loop over items
 };
 
 struct BwdArgs {
