@@ -517,20 +517,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 #endif
 }
 
-// Compute units of the current device (0 if it cannot be read), looked up
-// once per device.
-int cu_count() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, int grid, hipStream_t s) {
   if (a.cu_seqlens != nullptr)
@@ -541,6 +527,18 @@ hipError_t launch(const FwdArgs& a, int grid, hipStream_t s) {
 }
 
 }  // namespace
+
+int cu_count() {
+  static int cached[64] = {};   // per device; a racing first lookup writes the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 hipError_t launch_fwd_bf16(int d, int causal, FwdArgs a, int B, int H, hipStream_t s) {
   // The kernel needs c > 0 so that -inf scores stay -inf after scaling; a

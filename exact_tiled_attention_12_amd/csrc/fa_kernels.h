@@ -108,6 +108,10 @@ hipError_t launch_fwd_bf16(int d, int causal, FwdArgs a, int B, int H, hipStream
 // a fixed key-tile order and the preprocess pass also clears the counters.
 hipError_t launch_bwd(DType dt, int d, int causal, BwdArgs a, int B, int H, int stage_mask, hipStream_t s);
 hipError_t launch_bwd_bf16_main(int d, int causal, BwdArgs a, int B, int H, hipStream_t s);
+// Compute units of the current device (0 if it cannot be read), looked up
+// once per device.
+int cu_count();
+
 hipError_t launch_quant_fp8(int d, QuantArgs a, int B, int H, hipStream_t s);
 hipError_t launch_fwd_fp8(int d, int causal, Fp8FwdArgs a, int B, int H, hipStream_t s);
 hipError_t launch_dequant_fp8(const unsigned char* x8, const float* scales, void* out, int B, int H, int N, int d,
