@@ -38,6 +38,7 @@ from oracle import fp8 as F  # noqa: E402
 import seeded_inputs as si  # noqa: E402
 
 BLOCKS = (64, 128, 256, 1024, 0)
+REFERENCE = os.environ.get("FP8_REFERENCE", "pow2")   # the emulation's row reference (see fp8_attention_tiled)
 
 
 def sample_heads(x, w, n):
@@ -96,7 +97,8 @@ def one_head(args):
         q8, sq = quant_head(q, br, R, qk_form, amax["q"][rot])
         k8, sk = quant_head(k, br, R, qk_form, amax["k"][rot])
         v8, sv = quant_head(v, br, None, v_form, amax["v"][False])
-        o, _ = F.fp8_attention_tiled(q8, sq, k8, sk, v8, sv, w.scale, False, block_rows=br if br else 64)
+        o, _ = F.fp8_attention_tiled(q8, sq, k8, sk, v8, sv, w.scale, False, block_rows=br if br else 64,
+                                     reference=REFERENCE)
         out[(br, rot, form)] = float(np.sum((o[0, 0] - o_ex) ** 2)), o_ex.size
     return out
 

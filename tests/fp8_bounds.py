@@ -13,7 +13,13 @@ same steps on the same codes; they differ only in how the scores are formed:
 From a score error |dS_ij| <= delta_ij the bound follows the emulation's own
 steps:
   * the running maximum after each tile moves by at most delta_i = max_j
-    delta_ij;
+    delta_ij; with the power-of-two reference (the running maximum rounded
+    up to a whole power of two, reference="pow2" in the emulation) the
+    kernel may therefore round a maximum within delta_i of a power of two to
+    the neighbouring one: P' of that tile's keys then moves by an exact
+    factor of 2, which cancels against the factor 2 in the accumulator's
+    scale except in e4m3's subnormal range and at its top code, so both
+    references are taken as candidates there;
   * P' = 448 exp(S - m) therefore moves by a factor of at most
     exp(eta_i), eta_i = 2 delta_i;
   * its e4m3 code can be any code between those of P' exp(-eta_i) and
@@ -35,6 +41,7 @@ from oracle import fp8 as F
 EPS_MMA = 2.0 ** -11     # relative to the sum of absolute products
 EPS_MAX = 2.0 ** -10     # relative to the largest absolute product of one step
 U32 = 2.0 ** -24
+LN2 = float(np.log(2.0))
 
 
 def _bf16_half_ulp(x):
@@ -42,7 +49,7 @@ def _bf16_half_ulp(x):
     return np.exp2(np.floor(np.log2(a)) - 8)
 
 
-def bound_rows(q8, sq, k8, sk, v8, sv, scale, causal, rows, B_c=64):
+def bound_rows(q8, sq, k8, sk, v8, sv, scale, causal, rows, B_c=64, reference="pow2"):
     """Bounds for |O_gpu - O_emul| ([len(rows), d]) and |LSE_gpu - LSE_emul| ([len(rows)]).
 
     q8..sv are the codes and scales of one (batch, head): [N, d] and [ceil(N/64)].
@@ -75,8 +82,19 @@ def bound_rows(q8, sq, k8, sk, v8, sv, scale, causal, rows, B_c=64):
     tile_of = keys // B_c
     tmax = np.stack([s[:, t * B_c:(t + 1) * B_c].max(axis=1) for t in range(t_c)], axis=1)
     m_run = np.maximum.accumulate(tmax, axis=1)
+    alt = np.zeros_like(m_run)                      # the other candidate reference, in powers of two
+    if reference == "pow2":
+        with np.errstate(invalid="ignore"):
+            u = m_run / LN2                         # the running maximum in log2 units
+            r = np.ceil(u)
+            win = 1.5 * dmax[:, None] / LN2 + 1e-6
+            alt = np.where(u - (r - 1.0) <= win, -1.0, np.where(r - u <= win, 1.0, 0.0))
+            m_run = np.where(np.isfinite(m_run), r * LN2, m_run)
+    elif reference != "exact":
+        raise ValueError(reference)
     m_fin = m_run[:, -1]
-    m_at = m_run[:, tile_of]                        # running max in force for key j
+    m_at = m_run[:, tile_of]                        # reference in force for key j
+    alt_at = alt[:, tile_of]
     with np.errstate(invalid="ignore", over="ignore"):
         p = np.where(vis, np.exp(s - m_at), 0.0)     # P~ of the emulation
         w = np.where(vis, np.exp(m_at - m_fin[:, None]), 0.0)
@@ -85,6 +103,10 @@ def bound_rows(q8, sq, k8, sk, v8, sv, scale, causal, rows, B_c=64):
     e = np.exp(eta)[:, None]
     lo = F.e4m3_decode(F.e4m3_encode(np.minimum(p * 448.0 / e, 448.0)))
     hi = F.e4m3_decode(F.e4m3_encode(np.minimum(p * 448.0 * e, 448.0)))
+    # the neighbouring reference: P' times 2^-alt, its code times 2^alt
+    f = np.exp2(-alt_at)
+    lo = np.minimum(lo, F.e4m3_decode(F.e4m3_encode(np.minimum(p * f * 448.0 / e, 448.0))) / f)
+    hi = np.maximum(hi, F.e4m3_decode(F.e4m3_encode(np.minimum(p * f * 448.0 * e, 448.0))) / f)
     # weights of V_j in O: pq/448 * w / l; GPU: within the code range, with
     # the rescale factors and l each off by at most exp(eta) (plus summation)
     lsum = np.exp(eta + N * U32 * 4)[:, None]

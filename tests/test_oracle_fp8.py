@@ -154,42 +154,49 @@ def test_rotation_leaves_scores_unchanged_before_rounding():
     assert np.max(np.abs(s1 - s2)) <= 1e-4
 
 
-def test_fp8_emulation_without_p_rounding_is_exact_attention():
+@pytest.mark.parametrize("reference", ["pow2", "exact"])
+def test_fp8_emulation_without_p_rounding_is_exact_attention(reference):
     rng = np.random.default_rng(34)
     x = {n: rng.standard_normal((1, 2, 130, 16)) for n in "qkv"}
     qc = {n: F.quantize(x[n], 64) for n in "qkv"}
     for causal in (False, True):
         o, lse = F.fp8_attention_tiled(qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1],
                                        qc["v"][0], qc["v"][1], 0.25, causal, B_c=64,
-                                       quantize_p=False)
+                                       quantize_p=False, reference=reference)
         deq = {n: F.dequantize(qc[n][0], qc[n][1], 64) for n in "qkv"}
         o_ref, l_ref = A.forward(deq["q"], deq["k"], deq["v"], 0.25, causal)
         assert np.max(np.abs(o - o_ref)) <= 1e-12
         assert np.max(np.abs(lse - l_ref)) <= 1e-12
 
 
-def test_fp8_emulation_p_rounding_within_bound():
+@pytest.mark.parametrize("reference", ["pow2", "exact"])
+def test_fp8_emulation_p_rounding_within_bound(reference):
     """Rounding P~ * 448 to e4m3 moves each weight by at most half a step.
 
     |P8 - P~| <= 2^-4 P~ + 2^-10 / 448 per weight, so each O element moves by
-    at most (2^-4 + 2^-10 / 448 * n_keys / l) * max|v| (ratios with l >= 1).
-    The V rows are scaled per block so that the V block scales differ.
+    at most (2^-4 + 2^-10 / 448 * n_keys / l) * max|v|, where l, the sum of
+    P~ in the units of the final reference, is at least the maximum's own
+    P~: 1 with the exact maximum, at least 1/2 with the power-of-two
+    reference. The V rows are scaled per block so that the V block scales
+    differ.
     """
     rng = np.random.default_rng(35)
     x = {n: rng.standard_normal((1, 1, 192, 16)) for n in "qkv"}
     x["v"] *= np.repeat(np.array([1.0, 6.0, 0.5]), 64)[None, None, :, None]
     qc = {n: F.quantize(x[n], 64) for n in "qkv"}
     args = (qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1], qc["v"][0], qc["v"][1], 0.25, False)
-    o8, l8 = F.fp8_attention_tiled(*args, B_c=64, quantize_p=True)
-    o, l = F.fp8_attention_tiled(*args, B_c=64, quantize_p=False)
+    o8, l8 = F.fp8_attention_tiled(*args, B_c=64, quantize_p=True, reference=reference)
+    o, l = F.fp8_attention_tiled(*args, B_c=64, quantize_p=False, reference=reference)
     vmax = np.abs(F.dequantize(qc["v"][0], qc["v"][1], 64)).max()
-    bound = (2.0 ** -4 + 2.0 ** -10 / 448 * 192) * vmax
+    l_min = 1.0 if reference == "exact" else 0.5
+    bound = (2.0 ** -4 + 2.0 ** -10 / 448 * 192 / l_min) * vmax
     assert np.max(np.abs(o8 - o)) <= bound
     assert np.max(np.abs(o8 - o)) > 0          # the rounding is really applied
     assert np.array_equal(l8, l)                # l comes from the unrounded P~
 
 
-def test_fp8_emulation_v_scale_power_of_two_invariance():
+@pytest.mark.parametrize("reference", ["pow2", "exact"])
+def test_fp8_emulation_v_scale_power_of_two_invariance(reference):
     """Multiplying every V block scale by 2^k (same codes) multiplies O by 2^k exactly.
 
     P and its e4m3 codes do not depend on V, so only the dequantised V is
@@ -201,14 +208,17 @@ def test_fp8_emulation_v_scale_power_of_two_invariance():
     qc = {n: F.quantize(x[n], 64) for n in "qkv"}
     for causal in (False, True):
         base = (qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1], qc["v"][0])
-        o1, l1 = F.fp8_attention_tiled(*base, qc["v"][1], 0.3, causal)
-        o2, l2 = F.fp8_attention_tiled(*base, qc["v"][1] * np.float32(8.0), 0.3, causal)
+        o1, l1 = F.fp8_attention_tiled(*base, qc["v"][1], 0.3, causal, reference=reference)
+        o2, l2 = F.fp8_attention_tiled(*base, qc["v"][1] * np.float32(8.0), 0.3, causal, reference=reference)
         assert np.array_equal(o2, 8.0 * o1)
         assert np.array_equal(l2, l1)
 
 
-def test_bound_helper_rebuilds_the_emulation():
-    """tests/fp8_bounds.py rebuilds the emulation's O from its own weights; both must agree."""
+@pytest.mark.parametrize("reference", ["pow2", "exact"])
+def test_bound_helper_rebuilds_the_emulation(reference):
+    """tests/fp8_bounds.py rebuilds the emulation's O in closed form (each key's
+    weight from the reference in force at its tile, no running rescale); the
+    online emulation must agree."""
     import sys, os
     sys.path.insert(0, os.path.dirname(__file__))
     from fp8_bounds import bound_rows
@@ -218,12 +228,68 @@ def test_bound_helper_rebuilds_the_emulation():
     qc = {n: F.quantize(x[n], 64) for n in "qkv"}
     for causal in (False, True):
         o, lse = F.fp8_attention_tiled(qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1],
-                                       qc["v"][0], qc["v"][1], 0.25, causal)
+                                       qc["v"][0], qc["v"][1], 0.25, causal, reference=reference)
         rows = np.arange(200)
         _, _, o_em, l_em = bound_rows(qc["q"][0][0, 0], qc["q"][1][0, 0], qc["k"][0][0, 0], qc["k"][1][0, 0],
-                                      qc["v"][0][0, 0], qc["v"][1][0, 0], 0.25, causal, rows)
+                                      qc["v"][0][0, 0], qc["v"][1][0, 0], 0.25, causal, rows,
+                                      reference=reference)
         assert np.max(np.abs(o_em - o[0, 0])) <= 1e-12
         assert np.max(np.abs(l_em - lse[0, 0])) <= 1e-12
+
+
+def _hand_example(reference):
+    q8 = F.e4m3_encode(np.ones(3)).reshape(1, 1, 3, 1)      # three equal query rows
+    k8 = F.e4m3_encode(np.array([0.5, 2.0, 1.125])).reshape(1, 1, 3, 1)
+    v8 = F.e4m3_encode(np.array([1.0, -2.0, 0.5])).reshape(1, 1, 3, 1)
+    unit = np.ones((1, 1, 1), dtype=np.float32)
+    return F.fp8_attention_tiled(q8, unit, k8, unit, v8, unit, 1.0, False, B_c=1, reference=reference)
+
+
+def test_fp8_emulation_hand_example_power_of_two_reference():
+    """Queries all 1 (three equal rows), keys 0.5, 2.0, 1.125 (scores equal to them), values
+    1, -2, 0.5, one key per tile, worked by hand.
+
+    In log2 units the scores are 0.7213, 2.8854, 1.6231. The reference after
+    each tile is the running maximum rounded up to an integer: 1, 3, 3. P' =
+    448 * 2^(score - reference) = 369.31, 413.79, 172.49, whose nearest e4m3
+    values are 384, 416 and 176 (steps of 32 above 256, of 16 below). A key
+    weighs code * 2^reference / 448 against the unrounded denominator
+    e^0.5 + e^2 + e^1.125, so O = (768 - 6656 + 704) / 448 / (e^0.5 + e^2 +
+    e^1.125), and LSE is the log of that denominator.
+    """
+    o, lse = _hand_example("pow2")
+    den = np.exp(0.5) + np.exp(2.0) + np.exp(1.125)
+    assert np.max(np.abs(o[0, 0, :, 0] - (384 * 2 * 1.0 + 416 * 8 * -2.0 + 176 * 8 * 0.5) / 448 / den)) <= 1e-14
+    assert np.max(np.abs(lse[0, 0] - np.log(den))) <= 1e-14
+
+
+def test_fp8_emulation_hand_example_exact_reference():
+    """The same example with the exact running maximum: the first two keys are
+    each their tile's maximum, so P' = 448 exactly, and the third has P' =
+    448 e^(1.125 - 2) = 186.75, nearest e4m3 value 192; the earlier keys are
+    rescaled in float64 without rounding."""
+    o, lse = _hand_example("exact")
+    den = np.exp(0.5) + np.exp(2.0) + np.exp(1.125)
+    num = np.exp(0.5) * 1.0 + np.exp(2.0) * -2.0 + 192 / 448 * np.exp(2.0) * 0.5
+    assert np.max(np.abs(o[0, 0, :, 0] - num / den)) <= 1e-14
+    assert np.max(np.abs(lse[0, 0] - np.log(den))) <= 1e-14
+
+
+def test_fp8_reference_leaves_the_lse_unchanged():
+    """The row sum is kept in the units of whichever reference is in force and
+    rescaled exactly with it, so the LSE is the same for both references (and
+    equals that of the dequantised inputs); O differs only by P's rounding."""
+    rng = np.random.default_rng(39)
+    x = {n: rng.standard_normal((1, 2, 150, 16)) * 2.0 for n in "qkv"}
+    qc = {n: F.quantize(x[n], 64) for n in "qkv"}
+    args = (qc["q"][0], qc["q"][1], qc["k"][0], qc["k"][1], qc["v"][0], qc["v"][1], 0.25)
+    deq = {n: F.dequantize(qc[n][0], qc[n][1], 64) for n in "qkv"}
+    for causal in (False, True):
+        o1, l1 = F.fp8_attention_tiled(*args, causal, reference="pow2")
+        o2, l2 = F.fp8_attention_tiled(*args, causal, reference="exact")
+        _, l_ref = A.forward(deq["q"], deq["k"], deq["v"], 0.25, causal)
+        assert np.max(np.abs(l1 - l2)) <= 1e-12 and np.max(np.abs(l1 - l_ref)) <= 1e-12
+        assert np.max(np.abs(o1 - o2)) > 0
 
 
 @pytest.mark.parametrize("causal", [False, True])
