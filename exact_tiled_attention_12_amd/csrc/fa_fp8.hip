@@ -26,10 +26,16 @@
 //   * the scores are scaled by scale * log2(e) * sQ * sK_j in one FMA that
 //     also folds in the factor 448, so P' = 448 P~ comes out of exp2 ready to
 //     convert; l sums the float32 P' (the factor 448 cancels in O = acc / l);
-//   * the V block scale of each tile goes into its product with P as the
-//     matrix instruction's 8-bit exponent scale of the V operand, so the
-//     accumulator stays in the units of O; it is multiplied by alpha only in
-//     steps where some row's maximum moved, and O = acc / l at the end.
+//   * each row's reference m is its running maximum rounded up to a whole
+//     power of two (the lazy rescaling of "FlashAttention v1～v4 完整进化史",
+//     v4 part 3, kept inside e4m3's range: P' <= 448 still), so every factor
+//     between references is a power of two. The product of a tile's P with V
+//     carries two such factors as the matrix instruction's 8-bit exponent
+//     scales: the tile's V block scale on the V operand, and 2^(m - mr) on
+//     the P operand, per query row, where mr is the accumulator's own
+//     reference. The accumulator is multiplied only when m passes mr by more
+//     than 2^8 (in practice once per row, at its first key), and O = acc *
+//     2^(mr - m) / l at the end.
 #include <algorithm>
 #include <cfloat>
 #include <type_traits>
@@ -351,6 +357,10 @@ constexpr int kRB = kD;             // bytes per fp8 row
 constexpr int kTile = kBC * kRB;    // 8 KiB
 constexpr int kStage = 2 * kTile;   // K then V
 constexpr float kLog2_448 = 8.807354922057604f;
+// The accumulator is re-based when a row's reference m passes the
+// accumulator's reference mr by more than this (log2 units): it then holds
+// at most 448 * 2^8 times the sum of |P V| in the units of O.
+constexpr float kRebase = 8.f;
 
 #define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -374,10 +384,12 @@ __device__ __forceinline__ f32x16 mma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 // The same product with the A operand's blocks scaled by 2^(ea - 127) (an
-// 8-bit exponent, the biased exponent field of a power-of-two float) and
-// the B operand's by 2^0.
-__device__ __forceinline__ f32x16 mma_fp8_scale_a(i32x8 a, i32x8 b, f32x16 c, int ea) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, 127);
+// 8-bit exponent, the biased exponent field of a power-of-two float; one
+// value for the wave) and the B operand's by 2^(eb - 127), eb taken per
+// lane: lane l scales column l % 32 of B for the operand's 32-deep half
+// l / 32, so lanes l and l + 32 must pass the same eb to scale a column.
+__device__ __forceinline__ f32x16 mma_fp8_scale_ab(i32x8 a, i32x8 b, f32x16 c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
 
 
@@ -425,11 +437,12 @@ __device__ __forceinline__ void ring_barrier() {
 // step j (one 64-key tile) forms the softmax of tile j while the matrix cores
 // run S of tile j+1 and the product of tile j-1 with V; none of the step's 8
 // products depends on its vector work, so they are interleaved one product
-// at a time. The running maximum stays exact per tile (a stale maximum would
-// push 448 P past the e4m3 range). The V block scale of tile j-1 (a power
-// of two) scales the product of tile j-1 inside the matrix instruction, so
-// the accumulator is multiplied before that product only by alpha_{j-1}, and
-// only in steps where some row of the wave has alpha != 1.
+// at a time. The reference m never falls below the running maximum (a stale
+// maximum would push 448 P past the e4m3 range); it is that maximum rounded
+// up to a whole power of two. The V block scale of tile j-1 and 2^(m_{j-1} -
+// mr) (both powers of two) scale the product of tile j-1 inside the matrix
+// instruction, so the accumulator is multiplied only when a row's m moves
+// more than 2^8 past mr.
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -506,10 +519,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   const int vrow = 16 * (g16 >> 1) + (j16 >> 1);
   const unsigned v_lane = (unsigned)vrow * kRB + 16 * ((g16 & 1) ^ v_swz(vrow)) + 8 * (j16 & 1);
 
-  float m = -INFINITY;     // running maximum of this lane's row (scaled log2 units)
-  float l = 0.f;           // sum of P' = 448 P~ over this lane half's keys
-  float gam = 1.f;         // alpha of the newest softmax tile: the accumulator's factor
-  bool resc = false;       // gam != 1 on some lane of the wave
+  float m = -INFINITY;     // the row's reference: an integer >= its running maximum (scaled log2 units)
+  float l = 0.f;           // sum of P' = 448 P~ over this lane half's keys, in units of 2^m
+  float mr = -INFINITY;    // the accumulator's reference: an integer in [m - 8, m], or -inf before any key
   int ev = 127;            // 8-bit exponent of the V scale of the newest softmax tile
   f32x16 oacc[4];
 #pragma unroll
@@ -593,11 +605,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   // One pipeline step: softmax of tile j (raw scores sc, fp8 P to pc), S of
   // tile j+1 into sn, and O += V^T P^T of tile j-1 (pp, V operands from the
-  // step's fetches, V scaled by its block scale in the instruction).
-  // Accumulator block mt is multiplied by alpha of tile j-1 (gam from the
-  // previous step) at position mt, before its product at position 4 + mt,
-  // when that alpha is not 1 on some lane. mxr holds the raw row maximum of
-  // sc on entry (of the unmasked scores) and that of sn on exit.
+  // step's fetches, V scaled by its block scale and P by 2^(m - mr) in the
+  // instruction). mxr holds the raw row maximum of sc on entry (of the
+  // unmasked scores) and that of sn on exit.
   auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], const i32x8& pp, i32x8& pc, Ops& cur, Ops& nxt,
                   int kst, int vst, int nkst, int nvst, float skj, float svj_in, float& mxr) INL {
     if (masked(j)) {
@@ -610,22 +620,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     // c_j > 0 keeps masked scores at -inf after scaling (scale 0 or an
     // underflowing product would turn -inf * 0 into NaN).
     const float cj = fmaxf(cq * skj, FLT_MIN);
-    const float m_new = max3(m, mxr * cj, mxr * cj);
+    // P of tile j-1 enters the accumulator scaled by 2^(m - mr), m and mr as
+    // they stand before this step's update (any scale while the row has no
+    // key yet: that P is zero). Both lane halves hold the same m and mr.
+    const int eb_prev = m == -INFINITY ? 127 : 127 + (int)(m - mr);
+    const float cand = __builtin_ceilf(mxr * cj);
+    const float m_new = max3(m, cand, cand);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    const float gam_prev = gam;
-    const bool resc_prev = resc;
+    const float alpha = fast_exp2(m - m_use);      // a power of two (0 at the first key)
+    // Re-base at the row's first key (mr = -inf: the accumulator is still
+    // zero, factor 0) and when m passes mr by more than kRebase; NaN, so
+    // no re-base, while both are -inf.
+    const bool rebase = m_new - mr > kRebase;
+    const float g = rebase ? fast_exp2(mr - m_new) : 1.f;
+    mr = rebase ? m_new : mr;
     const int ev_prev = ev;
     m = m_new;
     l *= alpha;
     // P' = 2^(c_j s - m + log2 448) = 448 P~, four per position.
     const float nmo = kLog2_448 - m_use;
-    // alpha of tile j-1 on the accumulator, before its product with V
-    // below; skipped (most steps) when no row's maximum moved.
-    if (resc_prev) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) oacc[mt] *= gam_prev;
-    }
     f32x16 acc[2] = {f32x16{}, f32x16{}};
     float part[4];
     float hm0 = 0.f, hm1 = 0.f;
@@ -640,7 +653,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
         acc[tb] = mma_fp8(cur.kf[p], qf[ks], acc[tb]);
       } else {
         const int mt = p - 4;
-        oacc[mt] = mma_fp8_scale_a(cur.vf[mt], pp, oacc[mt], ev_prev);
+        oacc[mt] = mma_fp8_scale_ab(cur.vf[mt], pp, oacc[mt], ev_prev, eb_prev);
       }
       // Scores 4p .. 4p+3: word p of the fp8 P operand.
       float e[4];
@@ -660,8 +673,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       // Uniform bookkeeping, and the next tile's row maximum once its S
       // products (positions 0..3) have completed.
       if (p == 0) {
-        gam = alpha;
-        resc = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
         // (a drain step past the last tile has no V: its P is all zero)
         ev = j < kv_end ? (int)((__float_as_uint(svj_in) >> 23) & 0xFFu) : 127;
       }
@@ -673,6 +684,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     sn[0] = acc[0];
     sn[1] = acc[1];
     l += (part[0] + part[1]) + (part[2] + part[3]);
+    // The re-base, after tile j-1's product and before tile j's (next step).
+    if (__builtin_amdgcn_ballot_w64(rebase) != 0) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) oacc[mt] *= g;
+    }
   };
 
   // Ring bookkeeping, once every two steps, before step j (j even, j >= 2):
@@ -784,9 +800,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
     bad_v |= __builtin_amdgcn_ballot_w64(bad) != 0;
   }
 
-  // O = acc * sV / l' and LSE = (m + log2 l' - log2 448) ln 2.
+  // O = acc * 2^(mr - m) / l' and LSE = (m + log2 l' - log2 448) ln 2 (mr
+  // and m are finite whenever l' > 0).
   const float lt = halves_sum(l);
-  const float inv = bad_v ? __builtin_nanf("") : lt == 0.f ? 0.f : 1.f / lt;
+  const float inv = bad_v ? __builtin_nanf("") : lt == 0.f ? 0.f : fast_exp2(mr - m) / lt;
   if (qrow < N) {
     __bf16* og = (__bf16*)a.o + base + (size_t)qrow * kD;
 #pragma unroll
