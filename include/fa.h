@@ -272,8 +272,10 @@ FA_API int fa_quant_fp8(const void* x, const float* rot, unsigned char* x8, floa
  * 0: one per-tensor scale, broadcast to every entry); the dequantised value
  * of a code is decode(code) * s of its 64-row block. Other block_rows give
  * FA_ERR_UNSUPPORTED: the kernel's key tile is one 64-row scale block. Keys are taken
- * in tiles of 64 (one scale block each); m is the exact running maximum
- * after each tile, P~ = exp(S - m) <= 1 is rounded to e4m3 as
+ * in tiles of 64 (one scale block each); after each tile the row's
+ * reference m is its running maximum rounded up to a whole power of two
+ * (m = ln2 * an integer; the lazy rescaling of v4 part 3), P~ = exp(S - m)
+ * <= 1 is rounded to e4m3 as
  * e4m3(P~ * 448) for the product with V (dequantised by sv / 448 of its
  * tile), and the row sum l uses the float32 P~. Both products run on fp8
  * matrix cores into float32 accumulators; the V block scale enters the
