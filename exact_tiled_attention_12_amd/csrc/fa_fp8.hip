@@ -108,12 +108,29 @@ __device__ __forceinline__ float block_scale(float am, bool pow2) {
   return __uint_as_float(b);
 }
 
-// Four codes of y / s. With s a normal float32 at or above fl(amax / 448),
-// |y / s| <= 448 (1 + 2^-23) and the hardware conversion is exact (with a
-// power of two, y / s itself is exact); a subnormal s (a block of tiny
-// values) takes the saturating encoder.
-__device__ __forceinline__ uint32_t codes4(const float* y, float s, bool fast) {
-  if (fast) return e4m3x4(y[0] / s, y[1] / s, y[2] / s, y[3] / s);
+// The float32 quotient a / b rounded to nearest (the value a division
+// gives), from rb = RN(1 / b) by two corrections with the exact remainder
+// (Markstein's theorem: with rb = RN(1 / b) and q1 within one unit in the
+// last place of a / b, RN(q1 + (a - b q1) rb) is RN(a / b); q1, one
+// correction after a * rb, is within that). Valid without overflow or
+// underflow: callers have |a / b| <= 448 (1 + 2^-23) and b normal; quotients
+// that underflow are far below half the smallest e4m3 code, so their codes
+// do not depend on them. The sign is copied from a so that -0 stays -0.
+__device__ __forceinline__ float div_rn(float a, float b, float rb) {
+  const float q0 = a * rb;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, b, a), rb, q0);
+  const float q2 = __builtin_fmaf(__builtin_fmaf(-q1, b, a), rb, q1);
+  return __builtin_copysignf(q2, a);
+}
+
+// Four codes of y / s (rs = 1 / s). With s a normal float32 at or above
+// fl(amax / 448), |y / s| <= 448 (1 + 2^-23) and the hardware conversion is
+// exact; with s a power of two, y / s = y * rs exactly. A subnormal s (a
+// block of tiny values) takes the saturating encoder.
+__device__ __forceinline__ uint32_t codes4(const float* y, float s, float rs, bool fast, bool p2) {
+  if (fast && p2) return e4m3x4(y[0] * rs, y[1] * rs, y[2] * rs, y[3] * rs);
+  if (fast)
+    return e4m3x4(div_rn(y[0], s, rs), div_rn(y[1], s, rs), div_rn(y[2], s, rs), div_rn(y[3], s, rs));
   return e4m3_code(y[0] / s) | e4m3_code(y[1] / s) << 8 | e4m3_code(y[2] / s) << 16 | e4m3_code(y[3] / s) << 24;
 }
 
@@ -246,6 +263,8 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantArgs a, int nb
     }
 
     const bool fast = s >= kMinNormal;
+    const bool p2 = (__float_as_uint(s) & 0x007FFFFFu) == 0u;   // a power of two (s > 0)
+    const float rs = 1.f / s;
     const int rows = min(kQRows, N - blk * kQRows);
     unsigned char* x8 = a.x8 + ((size_t)bh * N + (size_t)blk * kQRows) * D;
     if constexpr (ROT) {
@@ -255,7 +274,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantArgs a, int nb
         if (row < rows) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            *(uint32_t*)(x8 + (size_t)row * D + 32 * ct + 8 * q + 4 * hh) = codes4(&y[16 * t + 4 * q], s, fast);
+            *(uint32_t*)(x8 + (size_t)row * D + 32 * ct + 8 * q + 4 * hh) = codes4(&y[16 * t + 4 * q], s, rs, fast, p2);
         }
       }
     } else {
@@ -265,8 +284,8 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantArgs a, int nb
         const int row = f / CH;
         if (row < rows) {
           u32x2 w;
-          w[0] = codes4(&y[8 * i], s, fast);
-          w[1] = codes4(&y[8 * i + 4], s, fast);
+          w[0] = codes4(&y[8 * i], s, rs, fast, p2);
+          w[1] = codes4(&y[8 * i + 4], s, rs, fast, p2);
           *(u32x2*)(x8 + (size_t)row * D + 8 * (f % CH)) = w;
         }
       }

@@ -86,6 +86,47 @@ def test_quant_exact(fa, block_rows, d, N, pow2):
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}"
 
 
+def _tie_block(s):
+    """One 64 x 128 block whose scale is exactly s (an element of 448 s) and
+    whose other elements are +-m s for every value m that lies halfway
+    between two adjacent e4m3 values (and for the e4m3 values themselves),
+    plus their bf16 neighbours: x / s then falls exactly on a rounding tie,
+    which the code must break to even as the oracle's float32 quotient does."""
+    vals = F.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    vals = np.unique(vals[np.isfinite(vals)])
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    base = np.concatenate([mids, vals]) * s
+    bits, exact = si.bf16_round(base.astype(np.float32))
+    assert np.array_equal(exact.astype(np.float64), base), "tie values must be exact in bf16"
+    nb = bits.astype(np.int32)
+    cand = np.concatenate([nb, nb + 1, nb - 1]).astype(np.uint16)
+    x = cand.view(np.int16).astype(np.int32) << 16
+    x = x.astype(np.uint32).view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) <= 448.0 * s)]
+    x = np.concatenate([x, -x])
+    out = np.resize(x, 64 * 128).astype(np.float32)
+    out[0] = np.float32(448.0 * s)
+    return out.reshape(64, 128)
+
+
+@pytest.mark.parametrize("s", [1.5, 1.25, 1.75, 0.75 * 2.0 ** -20, 1.25 * 2.0 ** 9])
+def test_quant_ties(fa, s):
+    """Codes of quotients that land exactly on e4m3 rounding ties, and next to
+    them, for scales that are not powers of two: bit-exact against the
+    oracle's codec of the float32 quotient."""
+    x = np.stack([_tie_block(s), _tie_block(s)[::-1]])[None]          # [1, 2, 64, 128]
+    xt, xv = _bf16_dev(x)
+    codes_ref, s_ref, _ = F.quantize(xv, 64)
+    assert float(s_ref[0, 0, 0]) == s
+    announce(f"fa_quant_fp8 ties s={s}")
+    x8, sc = fa.quant_fp8(xt, block_rows=64)
+    _sync()
+    got_c, got_s = x8.cpu().numpy(), sc.cpu().numpy()
+    assert np.array_equal(got_s.view(np.uint32), s_ref.view(np.uint32)), "scales differ"
+    bad = np.argwhere(got_c != codes_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}"
+
+
 @pytest.mark.parametrize("rotate", [False, True])
 def test_quant_nan_element(fa, rotate):
     """A NaN element gets a NaN code and is left out of its block's amax.
