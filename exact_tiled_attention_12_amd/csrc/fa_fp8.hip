@@ -108,29 +108,49 @@ __device__ __forceinline__ float block_scale(float am, bool pow2) {
   return __uint_as_float(b);
 }
 
-// The float32 quotient a / b rounded to nearest (the value a division
-// gives), from rb = RN(1 / b) by two corrections with the exact remainder
-// (Markstein's theorem: with rb = RN(1 / b) and q1 within one unit in the
-// last place of a / b, RN(q1 + (a - b q1) rb) is RN(a / b); q1, one
-// correction after a * rb, is within that). Valid without overflow or
-// underflow: callers have |a / b| <= 448 (1 + 2^-23) and b normal; quotients
-// that underflow are far below half the smallest e4m3 code, so their codes
-// do not depend on them. The sign is copied from a so that -0 stays -0.
-__device__ __forceinline__ float div_rn(float a, float b, float rb) {
-  const float q0 = a * rb;
-  const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, b, a), rb, q0);
-  const float q2 = __builtin_fmaf(__builtin_fmaf(-q1, b, a), rb, q1);
+// Divisor of a block in the form the quotients below take: s = bn * 2^-k
+// with bn in [1, 2), rn = RN(1 / bn); or, for s a power of two, rs = 1 / s
+// (exact).
+struct Divisor {
+  float bn, rn;
+  int k;
+  bool p2;
+};
+__device__ __forceinline__ Divisor make_divisor(float s) {
+  const uint32_t sb = __float_as_uint(s);
+  Divisor v;
+  v.p2 = (sb & 0x007FFFFFu) == 0u;
+  v.k = 127 - (int)((sb >> 23) & 0xFFu);
+  v.bn = __uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u);
+  v.rn = v.p2 ? 1.f / s : 1.f / v.bn;
+  return v;
+}
+
+// The float32 quotient a / s rounded to nearest (what a division gives), for
+// s normal and |a / s| <= 448 (1 + 2^-23). a and s are first scaled by the
+// same power of two (exactly) so that the divisor bn lies in [1, 2); then
+// from rn = RN(1 / bn) two corrections with the remainder: by Markstein's
+// theorem, with rn = RN(1 / bn) and q1 within one unit in the last place of
+// the quotient, RN(q1 + (a' - bn q1) rn) is RN(a' / bn), provided the
+// remainder does not underflow. Scaled, it underflows only for quotients
+// below about 2^-100, whose e4m3 code is 0 whatever their last bit (without
+// the scaling, a block of values near 2^-110 gave codes one step off at
+// rounding ties). The sign is copied from a so that -0 stays -0.
+__device__ __forceinline__ float div_rn(float a, const Divisor& v) {
+  const float an = __builtin_amdgcn_ldexpf(a, v.k);
+  const float q0 = an * v.rn;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, v.bn, an), v.rn, q0);
+  const float q2 = __builtin_fmaf(__builtin_fmaf(-q1, v.bn, an), v.rn, q1);
   return __builtin_copysignf(q2, a);
 }
 
-// Four codes of y / s (rs = 1 / s). With s a normal float32 at or above
-// fl(amax / 448), |y / s| <= 448 (1 + 2^-23) and the hardware conversion is
-// exact; with s a power of two, y / s = y * rs exactly. A subnormal s (a
-// block of tiny values) takes the saturating encoder.
-__device__ __forceinline__ uint32_t codes4(const float* y, float s, float rs, bool fast, bool p2) {
-  if (fast && p2) return e4m3x4(y[0] * rs, y[1] * rs, y[2] * rs, y[3] * rs);
-  if (fast)
-    return e4m3x4(div_rn(y[0], s, rs), div_rn(y[1], s, rs), div_rn(y[2], s, rs), div_rn(y[3], s, rs));
+// Four codes of y / s. With s a normal float32 at or above fl(amax / 448),
+// |y / s| <= 448 (1 + 2^-23) and the hardware conversion is exact; with s a
+// power of two, y / s = y * (1 / s) exactly. A subnormal s (a block of tiny
+// values) takes the division and the saturating encoder.
+__device__ __forceinline__ uint32_t codes4(const float* y, float s, const Divisor& v, bool fast) {
+  if (fast && v.p2) return e4m3x4(y[0] * v.rn, y[1] * v.rn, y[2] * v.rn, y[3] * v.rn);
+  if (fast) return e4m3x4(div_rn(y[0], v), div_rn(y[1], v), div_rn(y[2], v), div_rn(y[3], v));
   return e4m3_code(y[0] / s) | e4m3_code(y[1] / s) << 8 | e4m3_code(y[2] / s) << 16 | e4m3_code(y[3] / s) << 24;
 }
 
@@ -263,8 +283,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantArgs a, int nb
     }
 
     const bool fast = s >= kMinNormal;
-    const bool p2 = (__float_as_uint(s) & 0x007FFFFFu) == 0u;   // a power of two (s > 0)
-    const float rs = 1.f / s;
+    const Divisor dv = make_divisor(s);
     const int rows = min(kQRows, N - blk * kQRows);
     unsigned char* x8 = a.x8 + ((size_t)bh * N + (size_t)blk * kQRows) * D;
     if constexpr (ROT) {
@@ -274,7 +293,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantArgs a, int nb
         if (row < rows) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            *(uint32_t*)(x8 + (size_t)row * D + 32 * ct + 8 * q + 4 * hh) = codes4(&y[16 * t + 4 * q], s, rs, fast, p2);
+            *(uint32_t*)(x8 + (size_t)row * D + 32 * ct + 8 * q + 4 * hh) = codes4(&y[16 * t + 4 * q], s, dv, fast);
         }
       }
     } else {
@@ -284,8 +303,8 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantArgs a, int nb
         const int row = f / CH;
         if (row < rows) {
           u32x2 w;
-          w[0] = codes4(&y[8 * i], s, rs, fast, p2);
-          w[1] = codes4(&y[8 * i + 4], s, rs, fast, p2);
+          w[0] = codes4(&y[8 * i], s, dv, fast);
+          w[1] = codes4(&y[8 * i + 4], s, dv, fast);
           *(u32x2*)(x8 + (size_t)row * D + 8 * (f % CH)) = w;
         }
       }

@@ -127,6 +127,41 @@ def test_quant_ties(fa, s):
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}"
 
 
+# (amax, element) float32 bit patterns of bf16 values in blocks of tiny
+# magnitude (amax near 2^-105 .. 2^-112) whose quotient element / s falls on
+# an e4m3 rounding tie; found by a search with exact rational arithmetic, in
+# which a reciprocal-and-two-corrections quotient taken without scaling the
+# divisor first lands one unit below the tie (its remainder underflows) and
+# so one code lower.
+TINY_TIES = [(0x0B2A0000, 0x032A0000), (0x09AA0000, 0x01AA0000), (0x09BF0000, 0x01BF0000),
+             (0x09F80000, 0x02BA0000), (0x08A70000, 0x00A70000), (0x08AA0000, 0x00AA0000),
+             (0x08BF0000, 0x00BF0000), (0x08F80000, 0x01BA0000), (0x08F80000, 0x023A0000),
+             (0x08F80000, 0x02BA0000), (0x07980000, 0x00E40000), (0x07F80000, 0x00BA0000),
+             (0x07F80000, 0x013A0000), (0x07F80000, 0x01BA0000), (0x07F80000, 0x023A0000),
+             (0x07F80000, 0x02BA0000)]
+
+
+def test_quant_tiny_block_ties(fa):
+    """One 64-row block per pair: the element's code must be the oracle's
+    (the float32 quotient's tie broken to even)."""
+    P = len(TINY_TIES)
+    x = np.zeros((1, 1, 64 * P, 128), dtype=np.float32)
+    for p, (am, el) in enumerate(TINY_TIES):
+        x[0, 0, 64 * p, 0] = np.uint32(am).view(np.float32)
+        x[0, 0, 64 * p + 1, 0] = np.uint32(el).view(np.float32)
+        x[0, 0, 64 * p + 2, 0] = -np.uint32(el).view(np.float32)
+    xt, xv = _bf16_dev(x)
+    assert np.array_equal(xv, x), "the pairs are bf16 values"
+    codes_ref, s_ref, _ = F.quantize(xv, 64)
+    announce("fa_quant_fp8 tiny-block ties")
+    x8, sc = fa.quant_fp8(xt, block_rows=64)
+    _sync()
+    got_c, got_s = x8.cpu().numpy(), sc.cpu().numpy()
+    assert np.array_equal(got_s.view(np.uint32), s_ref.view(np.uint32)), "scales differ"
+    bad = np.argwhere(got_c != codes_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}: {got_c[tuple(bad[0])]} vs {codes_ref[tuple(bad[0])]}"
+
+
 @pytest.mark.parametrize("rotate", [False, True])
 def test_quant_nan_element(fa, rotate):
     """A NaN element gets a NaN code and is left out of its block's amax.
