@@ -118,7 +118,12 @@ __device__ __forceinline__ void ring_barrier() {
 
 // VARLEN: packed variable-length batch; a workgroup of a tile past its
 // sequence's end exits at once.
-template <int D, int W, bool CAUSAL, bool VARLEN>
+// SKIP (causal only): a wave stops computing once every block a step
+// touches lies above its rows, and from then on only issues its share of the
+// tile loads and keeps the barriers. It pays on short causal sequences,
+// where the diagonal tiles are a larger share of the work; on long ones the
+// branch's registers cost more than it saves.
+template <int D, int W, bool CAUSAL, bool VARLEN, bool SKIP>
 __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_bf16_kernel(FwdArgs a) {
   // The body is compiled in the device pass only: the host pass needs just the
   // launch stub, and its front end drops the stub of a kernel whose lambdas
@@ -468,6 +473,17 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_bf16_kernel(FwdArg
   // key (non-causal) or above the diagonal (causal), so the mask zeroes its
   // exponentials, and it completes the product of block U-1; the K it reads
   // (and the operands it fetches for a step U+1) are never used.
+  // Step u forms S of block u+1, P of block u and the product of block u-1
+  // with V; with this wave's last unmasked block wrow0 / 32 (causal), steps
+  // from wrow0 / 32 + 2 on add nothing to its rows.
+  const int skip_from = wrow0 / 32 + 2;
+  auto loads_only = [&](int ld_tile, auto ld_stage, auto ld_part) INL {
+    constexpr int LP = decltype(ld_part)::value;
+    if constexpr (LP >= 0) {
+      issue_load(ld_tile, ld_stage, LP, false);
+      issue_load(ld_tile, ld_stage, LP, true);
+    }
+  };
   auto one = [&](auto s_tag, int u0) INL -> bool {
     constexpr int S = decltype(s_tag)::value;
     const int u = u0 + S;
@@ -478,11 +494,18 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_bf16_kernel(FwdArg
     // Tile j+4 (j = (u-1)/2) goes to the stage freed at the last barrier.
     using LST = IC<(S / 2 + 4) % kStages>;
     const int lt = (u - 1) / 2 + 4;
+    const bool live = !SKIP || u < skip_from;
     if constexpr (S % 2 == 0) {
       tile_sync();
-      step(u, sb, sa, pa, pb, ob, oa, kt, vt, nkt, nvt, lt, LST{}, IC<0>{});
+      if (live)
+        step(u, sb, sa, pa, pb, ob, oa, kt, vt, nkt, nvt, lt, LST{}, IC<0>{});
+      else
+        loads_only(lt, LST{}, IC<0>{});
     } else {
-      step(u, sa, sb, pb, pa, oa, ob, kt, vt, nkt, nvt, lt, LST{}, IC<C::LPW == 2 ? 1 : -1>{});
+      if (live)
+        step(u, sa, sb, pb, pa, oa, ob, kt, vt, nkt, nvt, lt, LST{}, IC<C::LPW == 2 ? 1 : -1>{});
+      else
+        loads_only(lt, LST{}, IC<C::LPW == 2 ? 1 : -1>{});
     }
     return u == U;
   };
@@ -525,7 +548,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_bf16_kernel(FwdArg
 #endif
 }
 
-template <int D, int W, bool CAUSAL>
+template <int D, int W, bool CAUSAL, bool SKIP>
 hipError_t launch(FwdArgs a, int B, int H, hipStream_t s) {
   using C = Cfg<D, W>;
   // Packed variable-length batch: B sequences, tiles of the longest; one
@@ -543,10 +566,20 @@ hipError_t launch(FwdArgs a, int B, int H, hipStream_t s) {
     grid = n_cu;
   }
   if (a.cu_seqlens != nullptr)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, true>), dim3((int)grid), dim3(C::THREADS), 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, true, SKIP>), dim3((int)grid), dim3(C::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, false>), dim3((int)grid), dim3(C::THREADS), 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, false, SKIP>), dim3((int)grid), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
+}
+
+// Causal launches of sequences up to 4096 rows take the SKIP kernel
+// (measured: B=4 H=32 N=2048 0.161-0.164 against 0.169 ms, N=4096
+// 0.307-0.309 against 0.308-0.315 ms; N=16384 0.2-0.9% slower with it).
+template <int D, int W>
+hipError_t launch_mask(int causal, const FwdArgs& a, int B, int H, hipStream_t s) {
+  if (!causal) return launch<D, W, false, false>(a, B, H, s);
+  const int n = a.cu_seqlens != nullptr ? a.max_seqlen : a.N;
+  return n <= 4096 ? launch<D, W, true, true>(a, B, H, s) : launch<D, W, true, false>(a, B, H, s);
 }
 
 }  // namespace
@@ -574,11 +607,10 @@ hipError_t launch_fwd_bf16(int d, int causal, FwdArgs a, int B, int H, hipStream
     // causal 0.184 against 0.188 ms); beyond that the persistent 256-row
     // launch (N=16384: 1.12 against 1.15 ms).
     const long long items256 = (long long)B * H * (((a.cu_seqlens != nullptr ? a.max_seqlen : a.N) + 255) / 256);
-    if (items256 <= 4LL * cu_count())
-      return causal ? launch<64, 4, true>(a, B, H, s) : launch<64, 4, false>(a, B, H, s);
-    return causal ? launch<64, 8, true>(a, B, H, s) : launch<64, 8, false>(a, B, H, s);
+    if (items256 <= 4LL * cu_count()) return launch_mask<64, 4>(causal, a, B, H, s);
+    return launch_mask<64, 8>(causal, a, B, H, s);
   }
-  return causal ? launch<128, 8, true>(a, B, H, s) : launch<128, 8, false>(a, B, H, s);
+  return launch_mask<128, 8>(causal, a, B, H, s);
 }
 
 }  // namespace fa
