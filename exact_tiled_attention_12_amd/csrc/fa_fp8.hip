@@ -850,6 +850,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   // and m are finite whenever l' > 0).
   const float lt = halves_sum(l);
   const float inv = bad_v ? __builtin_nanf("") : lt == 0.f ? 0.f : fast_exp2(mr - m) / lt;
+  // The lane half, formed anew from the lane id (kept from the start, it
+  // took the register the loop needs most).
+  const int hh_e = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
   if (qrow < N) {
     __bf16* og = (__bf16*)a.o + base + (size_t)qrow * kD;
 #pragma unroll
@@ -859,9 +862,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
         u32x2 w;
         w[0] = pack_bf16x2(oacc[mt][4 * g + 0] * inv, oacc[mt][4 * g + 1] * inv);
         w[1] = pack_bf16x2(oacc[mt][4 * g + 2] * inv, oacc[mt][4 * g + 3] * inv);
-        *(u32x2*)(og + mt * 32 + 8 * g + 4 * hh) = w;
+        *(u32x2*)(og + mt * 32 + 8 * g + 4 * hh_e) = w;
       }
-    if (hh == 0)
+    if (hh_e == 0)
       a.lse[(size_t)bh * N + qrow] = bad_v ? __builtin_nanf("")
                                      : lt == 0.f ? -INFINITY : (m + fast_log2(lt) - kLog2_448) * kLn2;
   }
